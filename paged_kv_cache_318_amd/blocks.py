@@ -1,0 +1,157 @@
+"""Host-side block manager: free pool, per-sequence block tables, refcounts and copy-on-write.
+
+This is the bookkeeping that produces the device inputs of the paged path -- block tables,
+context lengths, the slot of each new token and the (src, dst) pairs a copy-on-write needs. It
+runs on the host and never touches device memory.
+
+Rules, by page title and section:
+
+* "PagedAttention", Ultralytics glossary, section "ページングの仕組み" (how paging works): a
+  sequence takes a new block from the free pool only once its previous block is full; the table
+  records the order of its blocks; only the tail of the last block is ever unused. The section's
+  example takes free blocks from the front of the free list -- ``BlockPool`` does the same.
+* Same page, section "シーケンス間でのブロック共有" (sharing blocks between sequences) and
+  section "関連手法" (continuous batching): several tables may name one physical block, counted
+  by a per-block reference count; a write into a block that another sequence also uses first
+  copies the block (copy-on-write); a finished sequence's blocks go straight back to the pool.
+* "vLLM и PagedAttention" (podcast transcript), paragraph on shared prefixes: the check is on the
+  reference count at the moment a sequence wants to add a token to a shared, partly filled block;
+  full shared blocks stay shared.
+* "Paged Attention" study notes, section "块分配策略" (block allocation): allocation fails with
+  an out-of-memory error when the free list is too short. Unlike those notes, ``free`` here
+  honours reference counts, and allocation never needs contiguous blocks.
+
+Readings where the pages are open: the sequence that triggers a copy gets the copy and the source
+block's count drops by one; the last remaining holder (count 1) writes in place; within one decode
+step sequences append in the order they are given.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["OutOfBlocks", "BlockPool"]
+
+
+class OutOfBlocks(RuntimeError):
+    """The free pool cannot satisfy an allocation; the pool state is left unchanged."""
+
+
+class BlockPool:
+    """Free list + reference counts + per-sequence tables for one pool of ``num_blocks`` blocks of
+    ``block_size`` token slots.
+
+    ``free_order`` gives the initial free list (front = next block handed out); by default it is
+    ``0 .. num_blocks-1``.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Iterable[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != sorted(set(order)) or any(b < 0 or b >= num_blocks for b in order):
+            raise ValueError("free_order must list distinct block ids in [0, num_blocks)")
+        self.free: deque = deque(order)
+        self.ref: List[int] = [0] * self.num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lengths: Dict[int, int] = {}
+
+    # -- allocation ---------------------------------------------------------------------------
+    def _take(self, n: int) -> List[int]:
+        if n > len(self.free):
+            raise OutOfBlocks(f"need {n} free blocks, have {len(self.free)}")
+        out = [self.free.popleft() for _ in range(n)]
+        for b in out:
+            self.ref[b] = 1
+        return out
+
+    def blocks_needed(self, num_tokens: int) -> int:
+        return -(-int(num_tokens) // self.block_size)
+
+    def add_sequence(self, seq_id: int, num_tokens: int) -> List[int]:
+        """Give a new sequence enough blocks for ``num_tokens`` tokens (its prompt)."""
+        if seq_id in self.tables:
+            raise ValueError(f"sequence {seq_id} already exists")
+        blocks = self._take(self.blocks_needed(num_tokens))
+        self.tables[seq_id] = blocks
+        self.lengths[seq_id] = int(num_tokens)
+        return list(blocks)
+
+    def fork(self, parent: int, child: int) -> None:
+        """``child`` starts as a copy of ``parent``'s table; every block gains one reference."""
+        if child in self.tables:
+            raise ValueError(f"sequence {child} already exists")
+        blocks = list(self.tables[parent])
+        for b in blocks:
+            self.ref[b] += 1
+        self.tables[child] = blocks
+        self.lengths[child] = self.lengths[parent]
+
+    def append_slot(self, seq_id: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """Reserve the slot of the sequence's next token.
+
+        Returns ``(slot, cow)`` where ``slot = block * block_size + offset`` and ``cow`` is a
+        ``(src, dst)`` pair when the token lands in a block shared with another sequence (that
+        block must be copied to ``dst`` before the token is written), else ``None``. On
+        ``OutOfBlocks`` the state is unchanged.
+        """
+        table = self.tables[seq_id]
+        pos = self.lengths[seq_id]
+        j, off = divmod(pos, self.block_size)
+        cow = None
+        if j == len(table):                       # previous block full (or none yet): new block
+            table.append(self._take(1)[0])
+        elif self.ref[table[j]] > 1:              # partly filled block shared with others: copy it
+            src = table[j]
+            dst = self._take(1)[0]
+            self.ref[src] -= 1
+            table[j] = dst
+            cow = (src, dst)
+        self.lengths[seq_id] = pos + 1
+        return table[j] * self.block_size + off, cow
+
+    def free_sequence(self, seq_id: int) -> None:
+        """Drop a finished sequence; blocks whose count reaches zero return to the free pool."""
+        for b in self.tables.pop(seq_id):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.lengths[seq_id]
+
+    # -- views ----------------------------------------------------------------------------------
+    def block_table(self, seq_ids: Sequence[int], width: Optional[int] = None) -> np.ndarray:
+        """``int32 [len(seq_ids)][width]`` tables, padded with -1."""
+        w = max((len(self.tables[s]) for s in seq_ids), default=0) if width is None else int(width)
+        out = np.full((len(seq_ids), max(w, 1)), -1, dtype=np.int32)
+        for i, s in enumerate(seq_ids):
+            t = self.tables[s]
+            if len(t) > out.shape[1]:
+                raise ValueError("width smaller than a table")
+            out[i, :len(t)] = t
+        return out
+
+    def context_lens(self, seq_ids: Sequence[int]) -> np.ndarray:
+        return np.array([self.lengths[s] for s in seq_ids], dtype=np.int32)
+
+    def blocks_in_use(self) -> int:
+        return self.num_blocks - len(self.free)
+
+    # -- invariants -----------------------------------------------------------------------------
+    def check(self) -> None:
+        """Raise AssertionError if any bookkeeping invariant is broken."""
+        refs = [0] * self.num_blocks
+        for s, t in self.tables.items():
+            assert len(t) == self.blocks_needed(self.lengths[s]), f"seq {s}: table/length mismatch"
+            for b in t:
+                refs[b] += 1
+        assert refs == self.ref, "reference counts differ from the number of table entries"
+        free = set(self.free)
+        assert len(free) == len(self.free), "a block appears twice in the free list"
+        used = {b for b in range(self.num_blocks) if self.ref[b] > 0}
+        assert not (free & used), "a referenced block is on the free list"
+        assert free | used == set(range(self.num_blocks)), "a block is neither free nor referenced"
