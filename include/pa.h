@@ -1,0 +1,186 @@
+/*
+ * pa.h -- C ABI of libpagedattn.so: paged KV cache and decode-step paged attention on MI355X
+ * (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [Ultralytics] "PagedAttention", Ultralytics glossary (Japanese):
+ *       "ページングの仕組み" (how paging works) -- fixed-size blocks (16 tokens by default) in one
+ *       shared pool, a per-request block table recording the order of the blocks, the attention
+ *       kernel fetching keys and values block by block through that table; its PyTorch example
+ *       writes each key into slot (pos mod B) of the block at table index (pos div B) and reads
+ *       the request back through the table.
+ *       "シーケンス間でのブロック共有" (sharing blocks between sequences) -- refcounted shared
+ *       blocks and copy-on-write of a block another sequence still uses.
+ *       "関連手法" (related methods) -- grouped-query attention and an 8-bit (FP8) KV cache.
+ *   [Wikipedia] "PagedAttention", Wikipedia article, section "Математическая формулировка"
+ *       (mathematical formulation) -- causal attention of query token i with the 1/sqrt(d)
+ *       scaling, and its blockwise form over blocks K_j, V_j of B tokens, j = 1..ceil(i/B).
+ *
+ * Data layout (all arrays row-major, C order):
+ *   k_cache  [num_blocks][num_kv_heads][block_size][head_dim]  key of slot o of block b, head g
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]  value of that slot, dim-major
+ *   k_scale, v_scale  float [num_blocks][num_kv_heads]          fp8 caches only: real value of a
+ *                                                                stored code c is e4m3(c) * scale
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]          physical block of logical block j
+ *   context_lens  int32 [num_seqs]                              tokens a sequence attends (L)
+ *   slot_mapping  int32 [num_tokens]                            block * block_size + offset
+ *   q, out        [num_seqs][num_heads][head_dim]
+ *   query head h reads kv head h / (num_heads / num_kv_heads).
+ *
+ * Element types: PA_F32 (IEEE binary32), PA_F16 (binary16), PA_BF16 (bfloat16 bit patterns),
+ * PA_FP8_E4M3 (OCP E4M3: bias 7, max 448, no infinities, S.1111.111 = NaN).
+ *
+ * Ownership: every pointer is caller-owned memory; device pointers are HIP device memory of the
+ * current device. The library never allocates or frees device memory; pa_decode takes a
+ * caller-supplied workspace. Calls only enqueue work on `stream` (a hipStream_t; NULL = the
+ * null stream) and return without synchronising.
+ *
+ * Errors: every scalar argument is checked on the host before any HIP call, so a bad call
+ * returns an error code and touches neither the device nor the stream. Device array *contents*
+ * (block ids, slots, lengths) are not validated; the kernels clamp them so that a bad entry can
+ * never make them read or write outside the arrays described above, but the result is then
+ * undefined. After the launches, a HIP launch error is reported as PA_ERR_HIP.
+ *
+ * Thread safety: the compute entry points hold no state and may be called concurrently; the
+ * profiling counters (pa_profile_*) are process-global and not synchronised.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, inconsistent shapes        */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim / block_size / dtype combination not built         */
+  PA_ERR_WORKSPACE = -3,   /* workspace smaller than pa_decode_workspace_bytes() asks for  */
+  PA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed                   */
+} pa_status;
+
+typedef enum {
+  PA_VARIANT_AUTO = 0, /* MFMA when num_heads > num_kv_heads and the cache is 16-bit or fp8   */
+  PA_VARIANT_VALU = 1, /* one work-group per query head: DPP dot products, any head grouping  */
+  PA_VARIANT_MFMA = 2  /* one work-group per kv head: the query group x block on MFMA        */
+} pa_variant;
+
+/* Human-readable name of a pa_status value (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int pa_version(void);
+
+/*
+ * pa_write_kv -- slot-mapped write of new tokens' keys and values into their blocks
+ * ([Ultralytics] "ページングの仕組み": the slot arithmetic of the example).
+ *
+ *   k_new, v_new  device, in_dtype  [num_tokens][num_kv_heads][head_dim]
+ *   k_cache, v_cache  device, cache_dtype, layout above (written)
+ *   slot_mapping  device int32 [num_tokens]; slot < 0 skips the token. Slots must be distinct.
+ *   cache_dtype == in_dtype (PA_F32 / PA_F16 / PA_BF16): the stored bits are the input bits.
+ *   cache_dtype == PA_FP8_E4M3 (in_dtype any 16/32-bit type): stored code = round-to-nearest-
+ *     even E4M3 of (float)x / scale[block][head] (one IEEE fp32 divide; scales must be positive),
+ *     magnitudes >= 448 saturate to 448, NaN stays NaN; the code's sign bit is x's sign bit.
+ *     k_scale / v_scale are read, not written.
+ *   head_dim in {64, 128}; block_size in {8, 16, 32}; num_blocks * block_size < 2^31.
+ */
+int pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                int block_size, int num_blocks, pa_dtype in_dtype, pa_dtype cache_dtype,
+                const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole blocks for copy-on-write ([Ultralytics]
+ * "シーケンス間でのブロック共有": a block still used by another sequence is copied before a
+ * write).
+ *
+ *   block_pairs  device int32 [num_pairs][2] = (src, dst). For each pair the dst block's keys
+ *   and values of every kv head (and, for fp8 caches, both scales) become a copy of src's.
+ *   The dsts must be distinct and no dst may also be a src in the same call (pairs are then
+ *   independent and run in parallel). num_pairs == 0 is a no-op.
+ *   k_scale / v_scale: required for PA_FP8_E4M3 caches, ignored otherwise.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, pa_dtype cache_dtype, void* stream);
+
+/*
+ * pa_gather_kv -- read sequences back through their block tables into contiguous arrays
+ * ([Ultralytics] "ページングの仕組み": the example's read-back through the table).
+ *
+ *   k_out, v_out  device, cache_dtype, [num_seqs][max_tokens][num_kv_heads][head_dim]
+ *   Row t of sequence s is written for t < min(context_lens[s], max_tokens) with the stored
+ *   bits of token t (values transposed back to dim-minor); other rows are left untouched.
+ *   max_tokens <= max_blocks_per_seq * block_size.
+ */
+int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                 int num_blocks, int max_tokens, pa_dtype cache_dtype, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- bytes of workspace pa_decode needs for these sizes (0 when no
+ * sequence can span more than one partition). partition_tokens as for pa_decode.
+ * Returns 0 as well for invalid sizes; pa_decode then reports the error.
+ */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                 int max_blocks_per_seq, int block_size, int partition_tokens);
+
+/*
+ * pa_decode -- decode-step paged attention ([Wikipedia] "Математическая формулировка"):
+ * for every sequence s and query head h,
+ *     out[s][h] = sum_{t < L} a_t v_t,   a_t = exp(scale q.k_t) / sum_{u < L} exp(scale q.k_u)
+ * with L = context_lens[s], keys/values of logical token t read from block
+ * block_tables[s][t / block_size] at slot t % block_size. Slots at or beyond L in the last block
+ * are excluded (their contents, NaN included, never reach the output); table entries at index
+ * >= ceil(L / block_size) are never read. L == 0 gives a zero output.
+ *
+ * Work is split into partitions of partition_tokens tokens (0 = library default; else a positive
+ * multiple of block_size); a sequence longer than one partition is combined by an exact
+ * log-sum-exp merge in a second kernel, using the workspace.
+ *
+ *   (q_dtype, cache_dtype): (F32, F32), (F16, F16), (BF16, BF16), (F16 | BF16, FP8_E4M3).
+ *   out_dtype: q_dtype or PA_F32. Accumulation is fp32 throughout.
+ *   k_scale / v_scale: required for fp8 caches (one scale per block and kv head).
+ *   num_heads % num_kv_heads == 0; head_dim in {64, 128}; block_size in {8, 16, 32}.
+ *   variant: pa_variant; PA_VARIANT_MFMA needs a 16-bit or fp8 cache, block_size 16 and at most
+ *   16 query heads per kv head.
+ *   workspace: device memory of at least pa_decode_workspace_bytes(...) bytes (may be NULL when
+ *   that is 0). Results are deterministic: the same inputs give the same bits, whatever the
+ *   physical placement of the blocks.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+              pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+              const float* v_scale, int partition_tokens, int variant, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling: when enabled, every pa_* launch is bracketed by HIP events on its stream.
+ * pa_profile_read synchronises on those events and returns, for one kernel kind, the summed
+ * device time in milliseconds and the number of launches since the last reset.
+ */
+typedef enum {
+  PA_KERNEL_DECODE_PARTITION = 0, /* the attention kernel (VALU or MFMA variant)      */
+  PA_KERNEL_DECODE_MERGE = 1,     /* the log-sum-exp merge of partitions              */
+  PA_KERNEL_WRITE_KV = 2,
+  PA_KERNEL_COPY_BLOCKS = 3,
+  PA_KERNEL_GATHER_KV = 4
+} pa_kernel_kind;
+
+int pa_profile_enable(int on);  /* also resets the counters */
+int pa_profile_read(int kernel_kind, double* total_ms, long long* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

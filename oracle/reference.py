@@ -105,10 +105,13 @@ def e4m3_encode(y) -> np.ndarray:
 
 
 def fp8_quantize(x, scale) -> np.ndarray:
-    """E4M3 code of ``x / scale``: the division is one IEEE float32 divide (round to nearest
-    even), then ``e4m3_encode``."""
-    y = np.asarray(x, dtype=np.float32) / np.asarray(scale, dtype=np.float32)
-    return e4m3_encode(y.astype(np.float32))
+    """E4M3 code of ``x / scale`` for a positive scale: the division is one IEEE float32 divide
+    (round to nearest even), the magnitude is rounded by ``e4m3_encode`` and the code's sign bit is
+    the sign bit of ``x`` (so a NaN input keeps its sign whatever the divide does to it)."""
+    x = np.asarray(x, dtype=np.float32)
+    y = (x / np.asarray(scale, dtype=np.float32)).astype(np.float32)
+    mag = e4m3_encode(np.abs(y)) & np.uint8(0x7F)
+    return (mag | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------------------------

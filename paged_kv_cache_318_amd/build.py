@@ -1,0 +1,73 @@
+"""Build ``libpagedattn.so`` in-tree with hipcc for gfx950 (cross-compiles without a GPU).
+
+    python -m paged_kv_cache_318_amd.build          # or: from paged_kv_cache_318_amd.build import build
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB_NAME = "libpagedattn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+SOURCES = ["pa_api.cpp", "kv_ops.hip", "decode_valu.hip", "decode_mfma.hip"]
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE (correctly rounded) fp32 division: the fp8 write divides by the block scale
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpagedattn)")
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source and link the shared library; always rebuilds. Returns its path."""
+    cc = hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([cc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+        outs = list(ex.map(_run, cmds))
+    tmp = LIB_PATH + ".tmp"
+    outs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,228 @@
+// Decode-step paged attention, VALU variant, and the partition merge kernel (gfx950).
+//
+// What is computed ("PagedAttention", Wikipedia article, section "Математическая формулировка"):
+// for the newest query token of sequence s and query head h, the causal softmax attention over
+// the L = context_lens[s] cached tokens, evaluated block by block as in the page's blockwise
+// form -- block j of B tokens read from the physical block block_tables[s][j] ("PagedAttention",
+// Ultralytics glossary, section "ページングの仕組み": the kernel follows the table block by
+// block). The blockwise denominator is one sum over all blocks; here it is accumulated as an
+// online (running-max) softmax, and partitions of a long sequence are combined by an exact
+// log-sum-exp merge, which regroups that same sum.
+//
+// Mapping (one work-group = 4 wave64s = one (query head, sequence, partition)):
+//   * wave w takes the partition's blocks w, w+4, w+8, ... (logical order fixed, so the result
+//     does not depend on where the blocks sit in the pool);
+//   * inside a wave, 16-lane row r owns tokens r*B/4 .. r*B/4 + B/4-1 of every block; lane c of
+//     the row owns key dims c*D/16 .. c*D/16 + D/16-1 (one 16-byte load per token for a 16-bit
+//     D=128 cache, so the four rows read 4 x 256 B per instruction) and value dims c, c+16, ...
+//     (values are dim-major in the block, so a lane reads the row's B/4 tokens of one dim);
+//   * q.k partial sums are reduced across the row with four DPP steps; each row keeps its own
+//     running max / sum / accumulator, merged with the other rows and waves through LDS at the
+//     end (the same merge algebra as across partitions).
+// Scores are kept in the log2 domain: z = (q.k) * scale * log2(e), weights exp2(z - max).
+// Tokens at or beyond L in the last block are excluded by selects (never by multiplying by 0),
+// so whatever sits in unused slots -- NaN included -- cannot reach the output.
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+template <int CDT, int QDT, int D, int B>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+  constexpr int EB = Elem<CDT>::bytes;
+  constexpr int QB = Elem<QDT>::bytes;
+  constexpr int DPL = D / 16;  // key dims per lane
+  constexpr int TPR = B / 4;   // tokens per 16-lane row
+  const int h = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane >> 4, c = lane & 15;
+  const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  const int nblk = (L + B - 1) / B;
+  const int b0 = p * a.part_blocks;
+  const size_t orow = (static_cast<size_t>(s) * Hq + h) * D;
+  if (b0 >= nblk) {
+    if (p == 0 && tid < D) store_out(a.out, orow + tid, 0.0f, a.out_dtype);  // L == 0
+    return;
+  }
+  const int b1 = min(nblk, b0 + a.part_blocks);
+  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const int g = h / (Hq / Hkv);
+
+  // query dims c*DPL .. c*DPL+DPL-1, as fp32
+  float qf[DPL];
+  {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + (orow + c * DPL) * QB;
+    Raw<DPL * QB> qr = load_raw<DPL * QB>(qp);
+    to_f32<QDT, DPL>(qr.w, qf);
+  }
+
+  float m = neg_inf(), l = 0.0f;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+
+  const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const size_t tile = static_cast<size_t>(B) * D * EB;  // bytes of one (block, head) tile
+  for (int j = b0 + wave; j < b1; j += 4) {
+    int pb = trow[j];
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
+    const uint8_t* kt = a.k_cache + base;
+    const uint8_t* vt = a.v_cache + base;
+
+    Raw<DPL * EB> kr[TPR];
+#pragma unroll
+    for (int i = 0; i < TPR; ++i)
+      kr[i] = load_raw<DPL * EB>(kt + ((r * TPR + i) * D + c * DPL) * EB);
+    Raw<TPR * EB> vr[DPL];
+#pragma unroll
+    for (int jj = 0; jj < DPL; ++jj)
+      vr[jj] = load_raw<TPR * EB>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
+
+    float zs = a.zscale;
+    float vs = 1.0f;
+    if constexpr (CDT == DT_FP8) {
+      zs *= a.k_scale[static_cast<size_t>(pb) * Hkv + g];
+      vs = a.v_scale[static_cast<size_t>(pb) * Hkv + g];
+    }
+    const int valid = L - j * B - r * TPR;  // tokens of this row below L (may be <= 0 or > TPR)
+
+    float z[TPR];
+#pragma unroll
+    for (int i = 0; i < TPR; ++i) {
+      float kf[DPL];
+      to_f32<CDT, DPL>(kr[i].w, kf);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
+      dot = row_sum16(dot);
+      z[i] = (i < valid) ? dot * zs : neg_inf();
+    }
+    float mt = z[0];
+#pragma unroll
+    for (int i = 1; i < TPR; ++i) mt = fmaxf(mt, z[i]);
+    const float mn = fmaxf(m, mt);
+    if (mn != neg_inf()) {  // a row that has seen no valid token yet keeps its empty state
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      float pz[TPR];
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TPR; ++i) {
+        pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
+        psum += pz[i];
+      }
+      l = l * alpha + psum;
+      m = mn;
+#pragma unroll
+      for (int jj = 0; jj < DPL; ++jj) {
+        float vf[TPR];
+        to_f32<CDT, TPR>(vr[jj].w, vf);
+        float t = acc[jj] * alpha;
+        float pv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) pv = __builtin_fmaf(pz[i], (i < valid) ? vf[i] : 0.0f, pv);
+        acc[jj] = __builtin_fmaf(pv, vs, t);
+      }
+    }
+  }
+
+  // merge the 16 row states (4 waves x 4 rows) of this work-group
+  __shared__ float sm_m[16], sm_l[16];
+  __shared__ float sm_acc[16][D + 1];
+  const int k = wave * 4 + r;
+  if (c == 0) {
+    sm_m[k] = m;
+    sm_l[k] = l;
+  }
+#pragma unroll
+  for (int jj = 0; jj < DPL; ++jj) sm_acc[k][c + 16 * jj] = acc[jj];
+  __syncthreads();
+  if (tid < D) {
+    float M = sm_m[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) M = fmaxf(M, sm_m[i]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float w = (sm_m[i] == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(sm_m[i] - M);
+      num = __builtin_fmaf(w, sm_acc[i][tid], num);
+      den = __builtin_fmaf(w, sm_l[i], den);
+    }
+    const float o = num / den;
+    if (nparts == 1) {
+      store_out(a.out, orow + tid, o, a.out_dtype);
+    } else {
+      const size_t pi = (static_cast<size_t>(s) * Hq + h) * a.max_parts + p;
+      a.ws_o[pi * D + tid] = o;
+      if (tid == 0) a.ws_ml[pi] = make_float2(M, den);
+    }
+  }
+}
+
+// One work-group of D threads per (query head, sequence): combines the sequence's partitions.
+// With per-partition maxima m_k, sums l_k and normalised outputs o_k (log2 domain):
+//   out = sum_k w_k o_k / sum_k w_k,   w_k = l_k * exp2(m_k - max_k m_k).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block_size) {
+  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.max_blocks * block_size ? a.max_blocks * block_size : L);
+  const int nblk = (L + block_size - 1) / block_size;
+  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+  if (nparts <= 1) return;
+  const size_t row = (static_cast<size_t>(s) * a.num_heads + h) * a.max_parts;
+  float M = neg_inf();
+  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_ml[row + k].x);
+  float num = 0.0f, den = 0.0f;
+  for (int k = 0; k < nparts; ++k) {
+    const float2 ml = a.ws_ml[row + k];
+    const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+    num = __builtin_fmaf(w, a.ws_o[(row + k) * D + d], num);
+    den += w;
+  }
+  store_out(a.out, (static_cast<size_t>(s) * a.num_heads + h) * D + d, num / den, a.out_dtype);
+}
+
+// ---- launchers ----------------------------------------------------------------------------------
+template <int CDT, int QDT, int D>
+static hipError_t launch_valu_b(const DecodeArgs& a, int B, dim3 grid, hipStream_t st) {
+  switch (B) {
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 8>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 16>), grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 32>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int CDT, int QDT>
+static hipError_t launch_valu_d(const DecodeArgs& a, int D, int B, dim3 grid, hipStream_t st) {
+  if (D == 64) return launch_valu_b<CDT, QDT, 64>(a, B, grid, st);
+  if (D == 128) return launch_valu_b<CDT, QDT, 128>(a, B, grid, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int cdt, int qdt, int D, int B, hipStream_t st) {
+  const dim3 grid(a.num_heads, a.num_seqs, a.max_parts);
+  if (cdt == DT_F32 && qdt == DT_F32) return launch_valu_d<DT_F32, DT_F32>(a, D, B, grid, st);
+  if (cdt == DT_F16 && qdt == DT_F16) return launch_valu_d<DT_F16, DT_F16>(a, D, B, grid, st);
+  if (cdt == DT_BF16 && qdt == DT_BF16) return launch_valu_d<DT_BF16, DT_BF16>(a, D, B, grid, st);
+  if (cdt == DT_FP8 && qdt == DT_F16) return launch_valu_d<DT_FP8, DT_F16>(a, D, B, grid, st);
+  if (cdt == DT_FP8 && qdt == DT_BF16) return launch_valu_d<DT_FP8, DT_BF16>(a, D, B, grid, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, int D, int B, hipStream_t st) {
+  const dim3 grid(a.num_heads, a.num_seqs);
+  if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, st, a, B);
+  else if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(128), 0, st, a, B);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

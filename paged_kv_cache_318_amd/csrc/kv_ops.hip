@@ -1,0 +1,196 @@
+// KV-cache moves on gfx950: slot-mapped write of new tokens, whole-block copy for
+// copy-on-write, and read-back of sequences through their block tables.
+//
+// "PagedAttention", Ultralytics glossary: section "ページングの仕組み" (how paging works) --
+// a token at position pos goes to slot pos mod B of the block the table lists at index pos div B,
+// and a request is read back through its table; section "シーケンス間でのブロック共有" (sharing
+// blocks between sequences) -- a block still used by another sequence is copied before a write.
+//
+// Layouts: k_cache [NB][Hkv][B][D] (a token's key is a contiguous row of D elements),
+// v_cache [NB][Hkv][D][B] (values are dim-major inside a block), fp8 scales [NB][Hkv].
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+template <int DT> struct Store;
+template <> struct Store<DT_F32> { using T = uint32_t; };
+template <> struct Store<DT_F16> { using T = uint16_t; };
+template <> struct Store<DT_BF16> { using T = uint16_t; };
+template <> struct Store<DT_FP8> { using T = uint8_t; };
+
+// |y| -> OCP E4M3 magnitude code, with the sign bit taken from x (the value before division by
+// the positive block scale, so a NaN quotient cannot lose its sign): round to nearest, ties to the
+// even mantissa; |y| >= 448 (and infinity) saturates to 448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y, float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  const float fa = __uint_as_float(a);
+  if (fa >= 448.0f) return sign | 0x7eu;
+  if (fa < 0.015625f) {
+    // below the smallest normal 2^-6 the codes step by 2^-9: scale by 2^9 (exact) and round half
+    // to even; a result of 8 is the smallest normal's code 0x08.
+    return sign | static_cast<uint32_t>(__builtin_rintf(fa * 512.0f));
+  }
+  // keep 3 mantissa bits of the fp32 pattern, rounding half to even at bit 20; a carry moves
+  // into the exponent, which is then rebiased from 127 to 7.
+  const uint32_t rnd = a + 0x7ffffu + ((a >> 20) & 1u);
+  return sign | ((((rnd >> 23) - 120u) << 3) | ((rnd >> 20) & 7u));
+}
+
+template <int IN_DT>
+__device__ __forceinline__ float load_as_f32(const void* p, size_t i) {
+  if constexpr (IN_DT == DT_F32) return reinterpret_cast<const float*>(p)[i];
+  else if constexpr (IN_DT == DT_F16) return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+// One work-group per new token; threads stride over its num_kv_heads x head_dim elements.
+template <int IN_DT, int C_DT>
+__global__ __launch_bounds__(256) void write_kv_kernel(const void* k_new, const void* v_new,
+                                                       void* k_cache, void* v_cache,
+                                                       const int32_t* slots, int Hkv, int D,
+                                                       int B, int NB, const float* k_scale,
+                                                       const float* v_scale) {
+  using CT = typename Store<C_DT>::T;
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= NB * B) return;  // skipped token (or an out-of-range slot: ignored)
+  const int b = slot / B, o = slot - (slot / B) * B;
+  const int n = Hkv * D;
+  CT* kc = reinterpret_cast<CT*>(k_cache);
+  CT* vc = reinterpret_cast<CT*>(v_cache);
+  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+    const int hh = idx / D, d = idx - (idx / D) * D;
+    const size_t src = static_cast<size_t>(t) * n + idx;
+    const size_t kdst = ((static_cast<size_t>(b) * Hkv + hh) * B + o) * D + d;
+    const size_t vdst = ((static_cast<size_t>(b) * Hkv + hh) * D + d) * B + o;
+    if constexpr (C_DT == DT_FP8) {
+      const float ks = k_scale[static_cast<size_t>(b) * Hkv + hh];
+      const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
+      const float xk = load_as_f32<IN_DT>(k_new, src);
+      const float xv = load_as_f32<IN_DT>(v_new, src);
+      kc[kdst] = static_cast<CT>(f32_to_e4m3(xk / ks, xk));
+      vc[vdst] = static_cast<CT>(f32_to_e4m3(xv / vs, xv));
+    } else {
+      kc[kdst] = reinterpret_cast<const CT*>(k_new)[src];
+      vc[vdst] = reinterpret_cast<const CT*>(v_new)[src];
+    }
+  }
+}
+
+// grid.x = pair, grid.y = chunk of the block; 16-byte copies of both caches.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* k_cache, uint8_t* v_cache,
+                                                          float* k_scale, float* v_scale,
+                                                          const int32_t* pairs, int NB,
+                                                          int Hkv, size_t block_bytes) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  const size_t n16 = block_bytes / 16;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache + static_cast<size_t>(src) * block_bytes);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache + static_cast<size_t>(src) * block_bytes);
+  u32x4* kd = reinterpret_cast<u32x4*>(k_cache + static_cast<size_t>(dst) * block_bytes);
+  u32x4* vd = reinterpret_cast<u32x4*>(v_cache + static_cast<size_t>(dst) * block_bytes);
+  for (size_t i = static_cast<size_t>(blockIdx.y) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.y) * blockDim.x) {
+    const u32x4 a = ks[i];
+    const u32x4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+  if (k_scale != nullptr && blockIdx.y == 0) {
+    for (int hh = threadIdx.x; hh < Hkv; hh += blockDim.x) {
+      k_scale[static_cast<size_t>(dst) * Hkv + hh] = k_scale[static_cast<size_t>(src) * Hkv + hh];
+      v_scale[static_cast<size_t>(dst) * Hkv + hh] = v_scale[static_cast<size_t>(src) * Hkv + hh];
+    }
+  }
+}
+
+// grid = (logical block j, sequence s); copies the block's valid tokens out in logical order.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kv_kernel(T* k_out, T* v_out, const T* k_cache,
+                                                        const T* v_cache, const int32_t* tables,
+                                                        const int32_t* lens, int Hkv, int D,
+                                                        int B, int MB, int NB, int max_tokens) {
+  const int j = blockIdx.x, s = blockIdx.y;
+  int L = lens[s];
+  L = L < 0 ? 0 : (L > MB * B ? MB * B : L);
+  L = L < max_tokens ? L : max_tokens;
+  const int t0 = j * B;
+  if (t0 >= L) return;
+  int pb = tables[static_cast<size_t>(s) * MB + j];
+  pb = pb < 0 ? 0 : (pb >= NB ? NB - 1 : pb);
+  const int nt = (L - t0) < B ? (L - t0) : B;
+  const int n = nt * Hkv * D;
+  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+    const int o = idx / (Hkv * D);
+    const int rem = idx - o * (Hkv * D);
+    const int hh = rem / D, d = rem - (rem / D) * D;
+    const size_t dst = (static_cast<size_t>(s) * max_tokens + t0 + o) * Hkv * D + rem;
+    k_out[dst] = k_cache[((static_cast<size_t>(pb) * Hkv + hh) * B + o) * D + d];
+    v_out[dst] = v_cache[((static_cast<size_t>(pb) * Hkv + hh) * D + d) * B + o];
+  }
+}
+
+// ---- launchers ----------------------------------------------------------------------------------
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* slots, int T, int Hkv, int D, int B, int NB, int in_dt,
+                           int cache_dt, const float* k_scale, const float* v_scale,
+                           hipStream_t st) {
+  const dim3 grid(T), block(256);
+#define PA_WRITE(I, C)                                                                         \
+  hipLaunchKernelGGL((write_kv_kernel<I, C>), grid, block, 0, st, k_new, v_new, k_cache,       \
+                     v_cache, slots, Hkv, D, B, NB, k_scale, v_scale)
+  if (cache_dt == DT_FP8) {
+    if (in_dt == DT_F32) PA_WRITE(DT_F32, DT_FP8);
+    else if (in_dt == DT_F16) PA_WRITE(DT_F16, DT_FP8);
+    else if (in_dt == DT_BF16) PA_WRITE(DT_BF16, DT_FP8);
+    else return hipErrorInvalidValue;
+  } else if (cache_dt == in_dt) {
+    if (in_dt == DT_F32) PA_WRITE(DT_F32, DT_F32);
+    else if (in_dt == DT_F16) PA_WRITE(DT_F16, DT_F16);
+    else if (in_dt == DT_BF16) PA_WRITE(DT_BF16, DT_BF16);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef PA_WRITE
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int num_pairs, int Hkv, int D, int B, int NB,
+                              int cache_dt, hipStream_t st) {
+  const int eb = cache_dt == DT_F32 ? 4 : (cache_dt == DT_FP8 ? 1 : 2);
+  const size_t block_bytes = static_cast<size_t>(Hkv) * B * D * eb;
+  const size_t n16 = block_bytes / 16;
+  int chunks = static_cast<int>((n16 + 2047) / 2048);  // ~8 16-byte copies per thread and cache
+  chunks = chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks);
+  const bool fp8 = cache_dt == DT_FP8;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, chunks), dim3(256), 0, st,
+                     reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                     fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, pairs, NB, Hkv,
+                     block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                            const int32_t* tables, const int32_t* lens, int S, int Hkv, int D,
+                            int B, int MB, int NB, int max_tokens, int cache_dt, hipStream_t st) {
+  const int mbt = (max_tokens + B - 1) / B;
+  const dim3 grid(mbt < MB ? mbt : MB, S), block(256);
+#define PA_GATHER(T)                                                                            \
+  hipLaunchKernelGGL((gather_kv_kernel<T>), grid, block, 0, st, reinterpret_cast<T*>(k_out),    \
+                     reinterpret_cast<T*>(v_out), reinterpret_cast<const T*>(k_cache),          \
+                     reinterpret_cast<const T*>(v_cache), tables, lens, Hkv, D, B, MB, NB,     \
+                     max_tokens)
+  if (cache_dt == DT_F32) PA_GATHER(uint32_t);
+  else if (cache_dt == DT_FP8) PA_GATHER(uint8_t);
+  else PA_GATHER(uint16_t);
+#undef PA_GATHER
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,287 @@
+// libpagedattn host side: the extern "C" entry points declared in include/pa.h.
+//
+// Every scalar argument is validated here before any HIP call, so a bad call returns an error
+// code without touching the device; then the call picks a kernel variant and enqueues it on the
+// caller's stream. The library allocates no device memory.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 512;
+constexpr int kMaxGridYZ = 65535;
+
+bool dtype_ok(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool block_size_ok(int b) { return b == 8 || b == 16 || b == 32; }
+
+// ---- profiling (process-global; events recorded around launches when enabled) -------------------
+struct EventPair {
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<EventPair> pending[5];
+  std::vector<EventPair> pool;
+  double ms[5] = {0, 0, 0, 0, 0};
+  long long count[5] = {0, 0, 0, 0, 0};
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+bool begin_event(hipStream_t st, EventPair* ev) {
+  Profiler& P = prof();
+  if (!P.on) return false;
+  if (!P.pool.empty()) {
+    *ev = P.pool.back();
+    P.pool.pop_back();
+  } else {
+    if (hipEventCreate(&ev->start) != hipSuccess) return false;
+    if (hipEventCreate(&ev->stop) != hipSuccess) return false;
+  }
+  return hipEventRecord(ev->start, st) == hipSuccess;
+}
+
+void end_event(bool active, hipStream_t st, const EventPair& ev, int kind) {
+  if (!active) return;
+  if (hipEventRecord(ev.stop, st) == hipSuccess) prof().pending[kind].push_back(ev);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : (dt == PA_FP8_E4M3 ? 1 : 2); }
+
+// Partition plan shared by workspace sizing and the launch.
+struct Plan {
+  int part_blocks;
+  int max_parts;
+};
+Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens) {
+  const int pt = partition_tokens > 0 ? partition_tokens : kDefaultPartitionTokens;
+  int pb = pt / block_size;
+  if (pb < 1) pb = 1;
+  return Plan{pb, (max_blocks_per_seq + pb - 1) / pb};
+}
+
+size_t workspace_for(int num_seqs, int num_heads, int head_dim, const Plan& pl) {
+  if (pl.max_parts <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_heads * pl.max_parts *
+         (static_cast<size_t>(head_dim) * sizeof(float) + 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype combination not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_version(void) { return 100; }
+
+int pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                int block_size, int num_blocks, pa_dtype in_dtype, pa_dtype cache_dtype,
+                const float* k_scale, const float* v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (in_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (cache_dtype != PA_FP8_E4M3 && cache_dtype != in_dtype) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  const bool timed = begin_event(st, &ev);
+  const hipError_t e = pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping,
+                                           num_tokens, num_kv_heads, head_dim, block_size,
+                                           num_blocks, in_dtype, cache_dtype, k_scale, v_scale, st);
+  end_event(timed, st, ev, PA_KERNEL_WRITE_KV);
+  return hip_status(e);
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int32_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, pa_dtype cache_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  const bool timed = begin_event(st, &ev);
+  const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, block_pairs,
+                                              num_pairs, num_kv_heads, head_dim, block_size,
+                                              num_blocks, cache_dtype, st);
+  end_event(timed, st, ev, PA_KERNEL_COPY_BLOCKS);
+  return hip_status(e);
+}
+
+int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                 int num_blocks, int max_tokens, pa_dtype cache_dtype, void* stream) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || max_tokens <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (max_tokens > max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
+  if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  const bool timed = begin_event(st, &ev);
+  const hipError_t e = pa::launch_gather_kv(k_out, v_out, k_cache, v_cache, block_tables,
+                                            context_lens, num_seqs, num_kv_heads, head_dim,
+                                            block_size, max_blocks_per_seq, num_blocks,
+                                            max_tokens, cache_dtype, st);
+  end_event(timed, st, ev, PA_KERNEL_GATHER_KV);
+  return hip_status(e);
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                                 int block_size, int partition_tokens) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 || partition_tokens < 0)
+    return 0;
+  return workspace_for(num_seqs, num_heads, head_dim,
+                       plan_partitions(max_blocks_per_seq, block_size, partition_tokens));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+              pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+              const float* v_scale, int partition_tokens, int variant, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
+  if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool pair_ok = (cache_dtype == q_dtype && q_dtype != PA_FP8_E4M3) ||
+                       (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
+  if (!pair_ok) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  const int G = num_heads / num_kv_heads;
+  const bool mfma_ok = cache_dtype != PA_F32 && block_size == 16 && G <= 16;
+  bool use_mfma;
+  if (variant == PA_VARIANT_MFMA) {
+    if (!mfma_ok) return PA_ERR_UNSUPPORTED;
+    use_mfma = true;
+  } else if (variant == PA_VARIANT_VALU) {
+    use_mfma = false;
+  } else {
+    use_mfma = mfma_ok && G >= 2;
+  }
+  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens);
+  if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(num_seqs, num_heads, head_dim, pl);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  const size_t o_bytes = need > 0 ? static_cast<size_t>(num_seqs) * num_heads * pl.max_parts *
+                                        head_dim * sizeof(float)
+                                  : 0;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = need > 0 ? reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + o_bytes) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.part_blocks = pl.part_blocks;
+  a.max_parts = pl.max_parts;
+  a.out_dtype = out_dtype;
+  a.zscale = scale * pa::kLog2e;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  bool timed = begin_event(st, &ev);
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, cache_dtype, q_dtype, head_dim, st)
+                          : pa::launch_decode_valu(a, cache_dtype, q_dtype, head_dim, block_size, st);
+  end_event(timed, st, ev, PA_KERNEL_DECODE_PARTITION);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (pl.max_parts > 1) {
+    timed = begin_event(st, &ev);
+    e = pa::launch_decode_merge(a, head_dim, block_size, st);
+    end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);
+  }
+  return hip_status(e);
+}
+
+int pa_profile_enable(int on) {
+  Profiler& P = prof();
+  for (int k = 0; k < 5; ++k) {
+    for (const EventPair& ev : P.pending[k]) P.pool.push_back(ev);
+    P.pending[k].clear();
+    P.ms[k] = 0.0;
+    P.count[k] = 0;
+  }
+  P.on = on != 0;
+  return PA_OK;
+}
+
+int pa_profile_read(int kernel_kind, double* total_ms, long long* launches) {
+  if (kernel_kind < 0 || kernel_kind > 4 || !total_ms || !launches) return PA_ERR_INVALID_ARG;
+  Profiler& P = prof();
+  for (const EventPair& ev : P.pending[kernel_kind]) {
+    if (hipEventSynchronize(ev.stop) != hipSuccess) return PA_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, ev.start, ev.stop) != hipSuccess) return PA_ERR_HIP;
+    P.ms[kernel_kind] += ms;
+    P.count[kernel_kind] += 1;
+    P.pool.push_back(ev);
+  }
+  P.pending[kernel_kind].clear();
+  *total_ms = P.ms[kernel_kind];
+  *launches = P.count[kernel_kind];
+  return PA_OK;
+}
+
+}  // extern "C"

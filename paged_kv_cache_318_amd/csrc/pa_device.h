@@ -1,0 +1,151 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedattn: element traits, raw vector
+// loads, storage <-> fp32 conversions, DPP row reductions, and the argument blocks the host
+// passes to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
+template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_FP8> { static constexpr int bytes = 1; };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// ---- raw loads of NB bytes (NB in {2, 4, 8, 16, 32, 64}); the address is NB-aligned (or
+// 16-aligned for NB >= 16) by construction of the layouts -------------------------------------
+template <int NB> struct Raw { uint32_t w[NB >= 4 ? NB / 4 : 1]; };
+
+template <int NB>
+__device__ __forceinline__ Raw<NB> load_raw(const void* p) {
+  Raw<NB> r;
+  if constexpr (NB == 2) {
+    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else if constexpr (NB == 4) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (NB == 8) {
+    u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    r.w[0] = v.x;
+    r.w[1] = v.y;
+  } else {
+    static_assert(NB % 16 == 0, "unsupported load width");
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      r.w[4 * i + 0] = v.x;
+      r.w[4 * i + 1] = v.y;
+      r.w[4 * i + 2] = v.z;
+      r.w[4 * i + 3] = v.w;
+    }
+  }
+  return r;
+}
+
+// ---- storage -> fp32 (all exact) -------------------------------------------------------------
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xffffu)));
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Converts N consecutive stored elements (packed little-endian in words w) to fp32.
+template <int DT, int N>
+__device__ __forceinline__ void to_f32(const uint32_t* w, float* f) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = __uint_as_float(w[i]);
+  } else if constexpr (DT == DT_F16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = f16_bits_to_f32(w[i / 2] >> (16 * (i & 1)));
+  } else if constexpr (DT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      f[i] = (i & 1) ? __uint_as_float(w[i / 2] & 0xffff0000u) : __uint_as_float(w[i / 2] << 16);
+  } else {
+    static_assert(DT == DT_FP8, "dtype");
+#pragma unroll
+    for (int wi = 0; wi < (N + 3) / 4; ++wi) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[wi]), false);
+      f[4 * wi] = lo.x;
+      if (4 * wi + 1 < N) f[4 * wi + 1] = lo.y;
+      if (4 * wi + 2 < N) {
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[wi]), true);
+        f[4 * wi + 2] = hi.x;
+        if (4 * wi + 3 < N) f[4 * wi + 3] = hi.y;
+      }
+    }
+  }
+}
+
+// ---- fp32 -> 16-bit storage ---------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// Stores one fp32 result as out_dtype (F32, F16 or BF16).
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v, int out_dtype) {
+  if (out_dtype == DT_F32) {
+    reinterpret_cast<float*>(out)[idx] = v;
+  } else if (out_dtype == DT_F16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_f16_rne(v));
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+  }
+}
+
+// ---- DPP reductions inside one 16-lane row -------------------------------------------------------
+// quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (swaps the two
+// quads of each 8-lane half), row_mirror (swaps the two halves): after the four steps every lane
+// of the row holds the same row-wide result (each step combines a value with its mirror image,
+// and + / max are commutative, so all lanes round identically).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+
+// ---- argument blocks ------------------------------------------------------------------------------
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* tables;
+  const int32_t* lens;
+  const float* k_scale;
+  const float* v_scale;
+  float* ws_o;     // [S][Hq][max_parts][D]
+  float2* ws_ml;   // [S][Hq][max_parts] = (max of log2-scaled scores, sum of exp2)
+  int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks;
+  int part_blocks, max_parts, out_dtype;
+  float zscale;    // softmax scale * log2(e)
+};
+
+}  // namespace pa

@@ -1,0 +1,31 @@
+// Internal launch entry points of libpagedattn (host side). Each enqueues its kernels on the
+// given stream and returns hipGetLastError(); all arguments were validated by pa_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,
+                              int block_size, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,
+                              hipStream_t st);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, hipStream_t st);
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int in_dt, int cache_dt,
+                           const float* k_scale, const float* v_scale, hipStream_t st);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int num_pairs, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks, int cache_dt,
+                              hipStream_t st);
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                            const int32_t* tables, const int32_t* lens, int num_seqs,
+                            int num_kv_heads, int head_dim, int block_size, int max_blocks,
+                            int num_blocks, int max_tokens, int cache_dt, hipStream_t st);
+
+}  // namespace pa

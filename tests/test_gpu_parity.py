@@ -1,0 +1,404 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on the same seeded
+inputs. Slot writes, block copies and gathers must be bit-exact; attention outputs must be within
+max-abs 1e-5 (fp32 cache), 2e-3 (fp16 / bf16 cache, fp32 accumulation) or 2e-2 (fp8 cache) of the
+oracle -- plus, for a 16-bit output, half an ulp of the output type at the reference value (the
+rounding every correct kernel has to make).
+
+Cases: the five decode-step configurations at full size (the shapes the bench times), small
+workloads that span several blocks, partitions and a ragged tail for every dtype / head grouping /
+head_dim / block size / kernel variant, and the edge cases: empty sequences, one-token sequences,
+unused slots poisoned with NaN, placement and partition-size invariance, determinism.
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_318_amd import lib
+from paged_kv_cache_318_amd.step import decode_step, workspace_for
+from workloads import config, make_workload, make_shared_prefix, round_to
+from workloads.device import to_numpy_f64, torch_dtype, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "fp8": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _half_ulp(x, dt):
+    if dt == "f32":
+        return np.zeros_like(x)
+    mant = {"f16": 10, "bf16": 7}[dt]
+    ax = np.maximum(np.abs(x), {"f16": 2.0 ** -14, "bf16": 2.0 ** -126}[dt])
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - mant - 1)
+
+
+def assert_close(got, want, cache_dt, out_dt, what=""):
+    assert got.shape == want.shape
+    tol = TOL[cache_dt] + _half_ulp(want, out_dt)
+    err = np.abs(got - want)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(np.isfinite(err), err, np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; max err "
+                             f"{np.nanmax(err):.3e} at {i} (got {got[i]}, want {want[i]})")
+    return float(err.max()) if err.size else 0.0
+
+
+def _host_after_step(w):
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    ks = None if w.k_scale is None else w.k_scale.copy()
+    vs = None if w.v_scale is None else w.v_scale.copy()
+    oracle.copy_blocks(kp, vp, w.cow, ks, vs)
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs)
+    return kp, vp, ks, vs
+
+
+def _check_inputs(w):
+    """Host-side bounds check of every index a kernel will follow."""
+    B, NB = w.block_size, w.num_blocks
+    for s in range(w.num_seqs):
+        nb = -(-int(w.lens[s]) // B)
+        assert nb <= w.tables.shape[1]
+        assert np.all((w.tables[s, :nb] >= 0) & (w.tables[s, :nb] < NB))
+    assert np.all(w.slots < NB * B)
+    assert np.all((w.cow >= 0) & (w.cow < NB))
+
+
+def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False):
+    _check_inputs(w)
+    d = upload(w)
+    out_dt = out_dt or w.q_dtype
+    out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(out_dt), device="cuda")
+    ws = workspace_for(d.q, d.tables, w.block_size, part)
+    decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
+                w.scale, d.k_scale, d.v_scale, partition_tokens=part, variant=variant, workspace=ws)
+    torch.cuda.synchronize()
+    res = to_numpy_f64(out)
+    if return_pools:
+        return res, d
+    return res
+
+
+def run_oracle(w, seqs=None):
+    kp, vp, ks, vs = _host_after_step(w)
+    return oracle.decode(w.q, kp, vp, w.tables, w.lens, w.block_size, w.scale, w.dtype, w.q_dtype,
+                         ks, vs, seqs=seqs)
+
+
+@functools.lru_cache(maxsize=None)
+def cfg(n, **kw):
+    return config(n, **kw)
+
+
+@functools.lru_cache(maxsize=None)
+def cfg_ref(n, **kw):
+    return run_oracle(cfg(n, **kw))
+
+
+# ----------------------------------------------------------------------------------------------
+# the five configurations at full size
+# ----------------------------------------------------------------------------------------------
+
+def test_config1_tiny_fp32():
+    w = cfg(1)
+    ref = cfg_ref(1)
+    assert_close(run_gpu(w), ref, "f32", "f32", "cfg1")
+    assert_close(run_gpu(w, part=16), ref, "f32", "f32", "cfg1 split")
+
+
+@pytest.mark.parametrize("out_dt", ["f16", "f32"])
+def test_config2_opt13b_mha_fp16(out_dt):
+    w = cfg(2)
+    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(2), "f16", out_dt, "cfg2")
+
+
+def test_config2_bf16_variant():
+    w = cfg(2, dtype="bf16")
+    assert_close(run_gpu(w, out_dt="f32"), cfg_ref(2, dtype="bf16"), "bf16", "f32", "cfg2 bf16")
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_config3_gqa_long_bf16(out_dt):
+    w = cfg(3)
+    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(3), "bf16", out_dt, "cfg3")
+
+
+def test_config3_valu_variant_agrees():
+    w = cfg(3)
+    assert_close(run_gpu(w, out_dt="f32", variant=lib.PA_VARIANT_VALU), cfg_ref(3), "bf16", "f32",
+                 "cfg3 valu")
+
+
+@pytest.mark.parametrize("first_step", [False, True])
+def test_config4_shared_prefix(first_step):
+    w = cfg(4, first_step=first_step)
+    if first_step:
+        assert w.cow.shape[0] > 0
+    got, d = run_gpu(w, out_dt="f32", return_pools=True)
+    assert_close(got, cfg_ref(4, first_step=first_step), "bf16", "f32", "cfg4")
+    kp, vp, _, _ = _host_after_step(w)
+    assert np.array_equal(d.k_cache.view(torch.int16).cpu().numpy().view(np.uint16), kp)
+    assert np.array_equal(d.v_cache.view(torch.int16).cpu().numpy().view(np.uint16), vp)
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_config5_fp8(out_dt):
+    w = cfg(5)
+    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(5), "fp8", out_dt, "cfg5")
+
+
+# ----------------------------------------------------------------------------------------------
+# small workloads: every dtype x grouping x head_dim x block size x variant
+# ----------------------------------------------------------------------------------------------
+
+SMALL_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 600, 1301)
+COMBOS = [
+    # cache, q, Hq, Hkv, D, B, variant
+    ("f32", "f32", 4, 4, 64, 16, 1), ("f32", "f32", 8, 2, 128, 16, 1), ("f32", "f32", 2, 2, 128, 8, 1),
+    ("f16", "f16", 4, 4, 128, 16, 1), ("f16", "f16", 4, 4, 64, 32, 1), ("bf16", "bf16", 6, 6, 128, 8, 1),
+    ("bf16", "bf16", 8, 2, 128, 16, 2), ("bf16", "bf16", 16, 2, 64, 16, 2), ("f16", "f16", 8, 1, 128, 16, 2),
+    ("bf16", "bf16", 32, 2, 128, 16, 2), ("bf16", "bf16", 4, 4, 128, 16, 2), ("f16", "f16", 6, 3, 128, 16, 0),
+    ("fp8", "bf16", 8, 2, 128, 16, 2), ("fp8", "f16", 8, 2, 64, 16, 2), ("fp8", "bf16", 4, 4, 128, 16, 1),
+    ("fp8", "f16", 4, 2, 128, 32, 1),
+]
+
+
+@pytest.mark.parametrize("cdt,qdt,hq,hkv,D,B,variant", COMBOS)
+@pytest.mark.parametrize("part", [0, 256])
+def test_small_parity(cdt, qdt, hq, hkv, D, B, variant, part):
+    if hq // hkv > 16 and variant == 2:
+        pytest.skip("the MFMA variant takes at most 16 query heads per kv head")
+    w = make_workload(list(SMALL_LENS), num_heads=hq, num_kv_heads=hkv, head_dim=D, block_size=B,
+                      dtype=cdt, q_dtype=qdt, seed=hq * 1000 + D + B)
+    got = run_gpu(w, out_dt="f32", part=part, variant=variant)
+    assert_close(got, run_oracle(w), cdt, "f32", f"{cdt}/{qdt} Hq={hq} Hkv={hkv} D={D} B={B} v={variant}")
+    if qdt != "f32":
+        got16 = run_gpu(w, out_dt=qdt, part=part, variant=variant)
+        assert_close(got16, run_oracle(w), cdt, qdt, "16-bit output")
+
+
+def test_mfma_rejects_more_than_16_heads_per_kv_head():
+    w = make_workload([5], num_heads=32, num_kv_heads=1, head_dim=64, dtype="bf16", seed=1)
+    with pytest.raises(lib.PagedAttnError):
+        run_gpu(w, variant=lib.PA_VARIANT_MFMA)
+    assert_close(run_gpu(w, out_dt="f32"), run_oracle(w), "bf16", "f32", "G=32 auto -> VALU")
+
+
+# ----------------------------------------------------------------------------------------------
+# edge cases and invariances
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_empty_and_single_token_sequences(variant):
+    w = make_workload([0, 1, 0, 3, 1], num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=9)
+    got = run_gpu(w, out_dt="f32", variant=variant)
+    assert np.all(got[0] == 0.0) and np.all(got[2] == 0.0)
+    ref = run_oracle(w)
+    assert_close(got, ref, "bf16", "f32", "edge")
+    # L == 1: the output is the new token's value exactly (bf16 -> fp32 is exact)
+    v1 = oracle.to_f64(w.v_new[1], "bf16")
+    assert np.array_equal(got[1], np.repeat(v1, 4, axis=0))
+
+
+def test_all_sequences_empty():
+    w = make_workload([0, 0, 0], num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16", seed=2)
+    got = run_gpu(w, out_dt="f32")
+    assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_placement_invariance_bit_exact(variant):
+    outs = []
+    for ps in (101, 202):
+        w = make_workload([3, 40, 333, 1000], num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                          seed=7, placement_seed=ps, free_fraction=1.0)
+        outs.append((run_gpu(w, out_dt="f32", variant=variant), w.tables.copy()))
+    assert not np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[0][0], outs[1][0])
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_poison_invariance_bit_exact(variant, dtype):
+    outs = []
+    for poison in ("nan", "big", "random", "zero"):
+        w = make_workload([5, 17, 250, 513], num_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
+                          seed=13, poison=poison)
+        outs.append(run_gpu(w, out_dt="f32", variant=variant, part=256))
+    assert np.all(np.isfinite(outs[0]))
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+
+
+def test_determinism_bit_exact():
+    w = cfg(3)
+    a = run_gpu(w, out_dt="f32")
+    b = run_gpu(w, out_dt="f32")
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("n", [2, 3, 5])
+def test_partition_size_invariance(n):
+    w = cfg(n, num_seqs=8) if n != 4 else cfg(4)
+    ref = run_oracle(w)
+    outs = [run_gpu(w, out_dt="f32", part=p) for p in (16, 256, 512, 1024)]
+    for o in outs:
+        assert_close(o, ref, w.dtype, "f32", f"cfg{n} partitions")
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= TOL[w.dtype]
+
+
+# ----------------------------------------------------------------------------------------------
+# fp8 conversions: every code decodes exactly; the write quantises bit-exactly
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_fp8_every_code_decodes_exactly(variant):
+    """L = 1, v_scale = 1: the output is the stored value code by code (all 254 finite codes)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    D = 128
+    w = make_workload([1, 1], num_heads=2, num_kv_heads=2, head_dim=D, dtype="fp8", q_dtype="bf16",
+                      seed=3)
+    w.slots[:] = -1                              # keep the pool as written below
+    for s, chunk in enumerate((codes[:D], codes[D - 2:])):
+        b = int(w.tables[s][0])
+        w.v_pool[b, :, :, 0] = chunk[None, :]
+        w.k_pool[b, :, 0, :] = 0x38              # key 1.0: any score, one token -> weight 1
+        w.v_scale[b] = 1.0
+        w.k_scale[b] = 1.0
+    got = run_gpu(w, out_dt="f32", variant=variant)
+    for s, chunk in enumerate((codes[:D], codes[D - 2:])):
+        assert np.array_equal(got[s], np.tile(oracle.e4m3_decode(chunk), (2, 1)))
+
+
+def _write_only(w, d):
+    lib.pa_write_kv(d.k_new, d.v_new, d.k_cache, d.v_cache, d.slots, d.k_scale, d.v_scale)
+    torch.cuda.synchronize()
+
+
+def _pool_np(t, dt):
+    if dt == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_write_kv_bit_exact(dt):
+    w = make_workload([1, 16, 17, 40, 100, 0], num_heads=4, num_kv_heads=4, head_dim=128,
+                      block_size=16, dtype=dt, seed=21)
+    d = upload(w)
+    _write_only(w, d)
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size)
+    assert np.array_equal(_pool_np(d.k_cache, dt).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_pool_np(d.v_cache, dt).view(np.uint8), vp.view(np.uint8))
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f16", "f32"])
+def test_write_kv_fp8_quantisation_bit_exact(in_dt):
+    """All 65536 bf16 patterns (NaN, inf, subnormals included), or random f16 / f32 values, through
+    the fp8 write under several per-(block, head) scales."""
+    Hkv, D, B = 2, 128, 16
+    T = 256
+    NB = T // B
+    if in_dt == "bf16":
+        x = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, D)
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+    else:
+        rng = np.random.default_rng(5)
+        xf = (rng.standard_normal((T, Hkv, D), dtype=np.float32) *
+              rng.choice([1e-4, 0.01, 1, 100, 1e4], size=(T, Hkv, 1)).astype(np.float32))
+        x = xf.astype(np.float16) if in_dt == "f16" else xf
+        xf = x.astype(np.float32)
+    rng = np.random.default_rng(6)
+    scales = rng.choice(np.array([1.0, 0.5, 2.0 ** -7, 0.0071, 3.3, 1e-3, 1.0 / 448], np.float32),
+                        size=(NB, Hkv)).astype(np.float32)
+    slots = rng.permutation(NB * B)[:T].astype(np.int32)
+    kc = torch.full((NB, Hkv, B, D), 0x55, dtype=torch.uint8, device="cuda")
+    vc = torch.full((NB, Hkv, D, B), 0x55, dtype=torch.uint8, device="cuda")
+    xin = torch.from_numpy(x.view(np.int16) if in_dt == "bf16" else x)
+    if in_dt == "bf16":
+        xin = xin.view(torch.bfloat16)
+    xin = xin.cuda()
+    ks = torch.from_numpy(scales).cuda()
+    vs = torch.from_numpy(scales[::-1].copy()).cuda()
+    lib.pa_write_kv(xin, xin, kc, vc, torch.from_numpy(slots).cuda(), ks, vs)
+    torch.cuda.synchronize()
+    kp = np.full((NB, Hkv, B, D), 0x55, np.uint8)
+    vp = np.full((NB, Hkv, D, B), 0x55, np.uint8)
+    for t in range(T):
+        b, o = divmod(int(slots[t]), B)
+        kp[b, :, o, :] = oracle.fp8_quantize(xf[t], scales[b][:, None])
+        vp[b, :, :, o] = oracle.fp8_quantize(xf[t], scales[::-1][b][:, None])
+    assert np.array_equal(kc.cpu().numpy(), kp)
+    assert np.array_equal(vc.cpu().numpy(), vp)
+
+
+# ----------------------------------------------------------------------------------------------
+# block copy and gather: bit-exact
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8", "f32"])
+def test_copy_blocks_bit_exact(dt):
+    w = make_workload([40, 77, 130], num_heads=8, num_kv_heads=8, head_dim=128, dtype=dt, seed=31,
+                      free_fraction=1.0)
+    d = upload(w)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(w.num_blocks)
+    pairs = np.stack([perm[:10], perm[10:20]], axis=1).astype(np.int32)   # distinct, disjoint
+    lib.pa_copy_blocks(d.k_cache, d.v_cache, torch.from_numpy(pairs).cuda(), d.k_scale, d.v_scale)
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    ks = None if w.k_scale is None else w.k_scale.copy()
+    vs = None if w.v_scale is None else w.v_scale.copy()
+    oracle.copy_blocks(kp, vp, pairs, ks, vs)
+    assert np.array_equal(_pool_np(d.k_cache, dt).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_pool_np(d.v_cache, dt).view(np.uint8), vp.view(np.uint8))
+    if ks is not None:
+        assert np.array_equal(d.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(d.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt,B", [("f16", 16), ("fp8", 32), ("f32", 8)])
+def test_gather_kv_bit_exact(dt, B):
+    w = make_workload([1, 16, 17, 90, 0], num_heads=4, num_kv_heads=4, head_dim=64, block_size=B,
+                      dtype=dt, seed=41)
+    d = upload(w)
+    _write_only(w, d)
+    kp, vp, _, _ = _host_after_step(w)
+    maxt = w.tables.shape[1] * B
+    ko = torch.zeros((w.num_seqs, maxt, 4, 64), dtype=d.k_cache.dtype, device="cuda")
+    vo = torch.zeros_like(ko)
+    lib.pa_gather_kv(ko, vo, d.k_cache, d.v_cache, d.tables, d.lens)
+    torch.cuda.synchronize()
+    kon, von = _pool_np(ko, dt), _pool_np(vo, dt)
+    for s in range(w.num_seqs):
+        L = int(w.lens[s])
+        K, V = oracle.gather_sequence(kp, vp, w.tables[s], L, B)
+        assert np.array_equal(kon[s, :L].view(np.uint8), K.view(np.uint8))
+        assert np.array_equal(von[s, :L].view(np.uint8), V.view(np.uint8))
+        assert not np.any(kon[s, L:].view(np.uint8))
+
+
+def test_profile_counts_launches():
+    w = cfg(1)
+    lib.pa_profile_enable(True)
+    run_gpu(w, part=16)
+    ms, n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
+    ms_m, n_m = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
+    ms_w, n_w = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
+    lib.pa_profile_enable(False)
+    assert (n, n_m, n_w) == (1, 1, 1)
+    assert ms > 0 and ms_m > 0 and ms_w > 0

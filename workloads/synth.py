@@ -195,10 +195,12 @@ def make_workload(lens, *, num_heads: int, num_kv_heads: int, head_dim: int, blo
                   num_blocks: Optional[int] = None, free_fraction: float = 0.2,
                   poison: str = "nan", table_width: Optional[int] = None,
                   scale: Optional[float] = None, name: str = "custom",
-                  lens_rng: Optional[np.random.Generator] = None) -> Workload:
+                  lens_rng: Optional[np.random.Generator] = None,
+                  placement_seed: Optional[int] = None) -> Workload:
     """Independent sequences with the given attended lengths (each >= 0; a length-0 sequence gets
     no new token). The pool holds ``num_blocks`` blocks (default: blocks in use + ``free_fraction``)
-    handed out in a seeded random order."""
+    handed out in a seeded random order. ``placement_seed`` draws that order from its own generator,
+    so two workloads differing only in it hold the same logical data at different physical blocks."""
     rng = lens_rng if lens_rng is not None else np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     S = lens.shape[0]
@@ -210,7 +212,7 @@ def make_workload(lens, *, num_heads: int, num_kv_heads: int, head_dim: int, blo
     NB = num_blocks if num_blocks is not None else max(1, math.ceil((1.0 + free_fraction) * used))
     if NB < used:
         raise ValueError(f"pool of {NB} blocks cannot hold {used} blocks")
-    perm = rng.permutation(NB)
+    perm = (rng if placement_seed is None else np.random.default_rng(placement_seed)).permutation(NB)
     pool = BlockPool(NB, B, free_order=perm.tolist())
     slots = np.full(S, -1, dtype=np.int32)
     for s in range(S):
