@@ -140,18 +140,23 @@ def to_f64(a, dtype: str) -> np.ndarray:
 
 
 def write_kv(k_pool, v_pool, k_new, v_new, slots, block_size, cache_dtype=None,
-             k_scale=None, v_scale=None):
+             k_scale=None, v_scale=None, in_dtype=None):
     """Token ``t`` with ``slots[t] >= 0`` goes to block ``slots[t] // B`` at offset
     ``slots[t] % B`` (the glossary example's slot arithmetic), for every kv head. With an fp8
-    cache the stored code is ``fp8_quantize(x, scale[block, head])``; otherwise the stored bits
-    are the new token's bits."""
+    cache the stored code is ``fp8_quantize(x, scale[block, head])`` of the new token's real
+    value ``x`` (its storage dtype ``in_dtype`` converted exactly to float32); otherwise the stored
+    bits are the new token's bits."""
     for t, slot in enumerate(np.asarray(slots).tolist()):
         if slot < 0:
             continue
         b, o = divmod(slot, block_size)
         if cache_dtype == "fp8":
-            k_pool[b, :, o, :] = fp8_quantize(k_new[t], k_scale[b][:, None])
-            v_pool[b, :, :, o] = fp8_quantize(v_new[t], v_scale[b][:, None])
+            if in_dtype not in ("f32", "f16", "bf16"):
+                raise ValueError("an fp8 write needs the new tokens' dtype (in_dtype)")
+            kx = to_f64(k_new[t], in_dtype).astype(np.float32)
+            vx = to_f64(v_new[t], in_dtype).astype(np.float32)
+            k_pool[b, :, o, :] = fp8_quantize(kx, k_scale[b][:, None])
+            v_pool[b, :, :, o] = fp8_quantize(vx, v_scale[b][:, None])
         else:
             k_pool[b, :, o, :] = k_new[t]
             v_pool[b, :, :, o] = v_new[t]

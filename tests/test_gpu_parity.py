@@ -61,7 +61,8 @@ def _host_after_step(w):
     ks = None if w.k_scale is None else w.k_scale.copy()
     vs = None if w.v_scale is None else w.v_scale.copy()
     oracle.copy_blocks(kp, vp, w.cow, ks, vs)
-    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs)
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs,
+                    w.new_dtype)
     return kp, vp, ks, vs
 
 

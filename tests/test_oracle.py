@@ -78,7 +78,8 @@ def _after_write(w):
     ks = None if w.k_scale is None else w.k_scale.copy()
     vs = None if w.v_scale is None else w.v_scale.copy()
     oracle.copy_blocks(kp, vp, w.cow, ks, vs)
-    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs)
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs,
+                    w.new_dtype)
     return kp, vp, ks, vs
 
 
@@ -374,3 +375,32 @@ def test_byte_model_matches_pages_memory_figures():
     assert round(m["params"] * 2 / 1e9) == g["weights_gb_approx"]
     # one layer of K+V for one token: the per-token unit the decode bench counts
     assert oracle.kv_bytes_per_token(1, 40, 128, 2) == 20480
+
+
+@pytest.mark.parametrize("in_dt", ["bf16", "f16", "f32"])
+def test_fp8_write_round_trips_within_half_a_code_step(in_dt):
+    """The fp8 write stores the code nearest to the input's real value divided by the block
+    scale: decoding it back is within half an E4M3 step (relative 2^-4, absolute 2^-10 below the
+    normal range) of x / scale, and saturates at 448."""
+    rng = np.random.default_rng(12)
+    Hkv, D, B, NB = 2, 16, 4, 6
+    x = rng.standard_normal((NB * B, Hkv, D), dtype=np.float32) * 3
+    x[0, 0, :4] = [1000.0, -1000.0, 0.0, -0.0]
+    stored = round_to(x, in_dt)
+    xr = oracle.to_f64(stored, in_dt)
+    scale = rng.uniform(0.002, 0.05, size=(NB, Hkv)).astype(np.float32)
+    kp = np.zeros((NB, Hkv, B, D), np.uint8)
+    vp = np.zeros((NB, Hkv, D, B), np.uint8)
+    slots = np.arange(NB * B)
+    oracle.write_kv(kp, vp, stored, stored, slots, B, "fp8", scale, scale, in_dt)
+    for t in slots:
+        b, o = divmod(int(t), B)
+        y = xr[t] / scale[b][:, None].astype(np.float64)
+        back_k = oracle.e4m3_decode(kp[b, :, o, :])
+        back_v = oracle.e4m3_decode(vp[b, :, :, o])
+        sat = np.abs(y) >= 448
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3), 2.0 ** -9)
+        for back in (back_k, back_v):
+            assert np.all(np.abs(back - y)[~sat] <= step[~sat] / 2 + 1e-12)
+            assert np.all(back[sat] == np.sign(y[sat]) * 448.0)
+            assert np.all(np.signbit(back) == np.signbit(xr[t]))
