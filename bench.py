@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is the whole hot path for one layer over one batch: copy-on-write block copies (when the
+workload has any), the slot-mapped write of every sequence's new token, then decode attention
+through the block tables (partition kernel + merge). The default workload is the OPT-13B-shaped
+MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
+uniform in [128, 2048], blocks scattered through a pool with 20% free blocks.
+
+Inputs are uploaded before timing (``--replicas`` independent copies of the pools, rotated step by
+step, so no step finds the previous step's data in the L2 or the MALL). The timed region is
+bracketed by device synchronisation; the library records HIP events around its own launches on
+the same stream, which gives the average duration of the attention kernel for the roofline.
+
+Prints one JSON line. ``value`` is algorithmic bytes of the step / step time (GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak), attended tokens/s"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline batch)")
+    p.add_argument("--dtype", default=None, help="override the cache dtype of config 2 (f16|bf16)")
+    p.add_argument("--first-step", action="store_true", help="config 4: every sample at its first step")
+    p.add_argument("--replicas", type=int, default=4)
+    p.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    p.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also launch one plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (as it stands) on host cores, over a bounded sample of the same workload:
+    whole sequences in order until the time budget is spent, BLAS limited to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    ks = None if w.k_scale is None else w.k_scale.copy()
+    vs = None if w.v_scale is None else w.v_scale.copy()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.copy_blocks(kp, vp, w.cow, ks, vs)
+        oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs, w.new_dtype)
+        done, tokens = 0, 0
+        while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
+            oracle.decode(w.q, kp, vp, w.tables, w.lens, w.block_size, w.scale, w.dtype, w.q_dtype,
+                          ks, vs, seqs=[done])
+            tokens += int(w.lens[done])
+            done += 1
+        dt = time.perf_counter() - t0
+    per_tok = w.kv_bytes() / max(w.attended_tokens, 1)
+    gbs = tokens * per_tok / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "attended_tokens_per_s": round(tokens / dt, 1),
+            "sample": f"write of all {w.num_seqs} new tokens + decode of the first {done} of "
+                      f"{w.num_seqs} sequences ({tokens} attended tokens x {w.num_heads} heads), "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the paged decode path here has no multi-GPU leg; see the design notes on sharding.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_318_amd import lib
+    from paged_kv_cache_318_amd.step import decode_step, workspace_for
+    from workloads import config
+    from workloads.device import torch_dtype, upload
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    lib.load()
+    over = {}
+    if args.dtype:
+        over["dtype"] = args.dtype
+    if args.first_step:
+        over["first_step"] = True
+    t_gen = time.perf_counter()
+    w = config(args.config, **over)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] workload {w.name}: {w.num_seqs} seqs, {w.attended_tokens} attended tokens, "
+          f"{w.kv_bytes() / 1e9:.3f} GB K/V per call, generated in {t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+
+    reps = [upload(w) for _ in range(max(1, args.replicas))]
+    out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(w.q_dtype), device="cuda")
+    ws = workspace_for(reps[0].q, reps[0].tables, w.block_size, args.partition)
+
+    def step(i):
+        d = reps[i % len(reps)]
+        decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
+                    d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
+                    variant=args.variant, workspace=ws)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup of {args.warmup} steps done", file=sys.stderr, flush=True)
+
+    lib.pa_profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    k_ms, k_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
+    m_ms, m_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
+    w_ms, w_n = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
+    c_ms, c_n = lib.pa_profile_read(lib.PA_KERNEL_COPY_BLOCKS)
+    lib.pa_profile_enable(False)
+    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    k_avg_ms = k_ms / max(k_n, 1)
+    unique = args.config == 4
+    dec_bytes = w.decode_bytes(unique=unique)
+    achieved = dec_bytes / (k_avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q, scattered blocks; no dataset)",
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "attended_tokens_per_s": round(w.attended_tokens / (ms_step * 1e-3), 1),
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "cache_dtype": w.dtype, "q_dtype": w.q_dtype, "accumulate": "f32",
+            "attended_tokens": w.attended_tokens, "num_blocks": w.num_blocks,
+            "cow_pairs": int(w.cow.shape[0]), "step_bytes": step_bytes,
+            "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
+            "replicas": len(reps), "partition_tokens": args.partition, "variant": args.variant,
+        },
+        "kernels_us": {
+            "decode_partition": round(1e3 * k_avg_ms, 2),
+            "decode_merge": round(1e3 * m_ms / max(m_n, 1), 2) if m_n else None,
+            "write_kv": round(1e3 * w_ms / max(w_n, 1), 2) if w_n else None,
+            "copy_blocks": round(1e3 * c_ms / max(c_n, 1), 2) if c_n else None,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode partition kernel", "bytes_per_launch": dec_bytes,
+            "bytes_basis": "unique" if unique else "logical",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
