@@ -43,6 +43,7 @@ def parse_args():
     p.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     p.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
@@ -78,6 +79,57 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"write of all {w.num_seqs} new tokens + decode of the first {done} of "
                       f"{w.num_seqs} sequences ({tokens} attended tokens x {w.num_heads} heads), "
                       f"fp64 numpy, {dt:.1f} s"}
+
+
+def read_ceiling(lib, tile_bytes: int, total_bytes: int = 4 << 30, reps: int = 5):
+    """Read rate this GPU sustains for tiles of the attention kernel's size: whole 4 GiB buffer,
+    tiles in address order and in a random order (the paged pattern), best of ``reps``."""
+    import torch
+    n = total_bytes // tile_bytes
+    buf = torch.empty(n * tile_bytes, dtype=torch.uint8, device="cuda")
+    order = torch.randperm(n, device="cuda", dtype=torch.int32)
+    sink = torch.empty(64 * 1024, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, o in (("linear", None), ("scattered", order)):
+        lib.pa_diag_read_bandwidth(buf, tile_bytes, n, o, sink)
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            lib.pa_diag_read_bandwidth(buf, tile_bytes, n, o, sink)
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        res[name] = round(n * tile_bytes / (best * 1e-3) / 1e9, 1)
+    res["tile_bytes"] = tile_bytes
+    return res
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """First 16 hex digits of sha256 over the sources the attention kernel is built from."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_318_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("pa_device.h", "decode_valu.hip" if kernel == "decode_valu" else "decode_mfma.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (fetch + write) from the committed counter summary, or None when it has
+    no entry for this kernel and workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    src = kernel_source_hash(kernel)
+    for line in open(path, encoding="utf-8"):
+        if line.startswith("#") or "=" not in line:
+            continue
+        kv = dict(tok.split("=", 1) for tok in line.split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source") == src:
+            return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+    return None
 
 
 def main():
@@ -134,7 +186,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup of {args.warmup} steps done", file=sys.stderr, flush=True)
 
-    lib.pa_profile_enable(True)
+    # timed region: K steps, nothing else on the stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -143,6 +195,14 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
+    # the same K steps again with the library's HIP events around every launch (kernel durations)
+    lib.pa_profile_enable(True)
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step_profiled = start.elapsed_time(end) / args.steps
     k_ms, k_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
     m_ms, m_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
     w_ms, w_n = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
@@ -153,6 +213,10 @@ def main():
     step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
     k_avg_ms = k_ms / max(k_n, 1)
+    G = w.num_heads // w.num_kv_heads
+    mfma_ok = w.dtype != "f32" and w.block_size == 16 and G <= 16
+    kernel = "decode_mfma" if (args.variant == 2 or (args.variant == 0 and mfma_ok and G >= 2)) \
+        else "decode_valu"
     unique = args.config == 4
     dec_bytes = w.decode_bytes(unique=unique)
     achieved = dec_bytes / (k_avg_ms * 1e-3) / 1e9
@@ -181,6 +245,7 @@ def main():
             "replicas": len(reps), "partition_tokens": args.partition, "variant": args.variant,
         },
         "kernels_us": {
+            "step_with_events": round(1e3 * ms_step_profiled, 2),
             "decode_partition": round(1e3 * k_avg_ms, 2),
             "decode_merge": round(1e3 * m_ms / max(m_n, 1), 2) if m_n else None,
             "write_kv": round(1e3 * w_ms / max(w_n, 1), 2) if w_n else None,
@@ -188,12 +253,19 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "decode partition kernel", "bytes_per_launch": dec_bytes,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(kernel, w.name),
+            "kernel": kernel, "bytes_per_launch": dec_bytes,
             "bytes_basis": "unique" if unique else "logical",
         },
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        del reps
+        ceil = read_ceiling(lib, w.block_size * w.head_dim * (1 if w.dtype == "fp8" else 2) *
+                            (2 if w.dtype == "f32" else 1))
+        line["read_ceiling_gbs"] = ceil
+        line["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["scattered"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

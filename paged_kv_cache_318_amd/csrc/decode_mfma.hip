@@ -8,17 +8,25 @@
 //     Z^T[16 tokens][G heads]  = K_tile[16][D] . Q_g^T[D][G]        (scores)
 //     O^T[D][G]               += V_tile^T[D][16] . P^T[16][G]        (weighted values)
 // One work-group (4 wave64s) handles one (kv head, sequence, partition); wave w takes blocks
-// w, w+4, ... of the partition, so each K/V tile is fetched from HBM once for all G heads.
+// w, w+4, ... of the partition, two per iteration, so each K/V tile is fetched from HBM once for
+// all G heads and every wave keeps two tiles (16 KB at 16 bits) in flight.
 //
-// Operand layouts (v_mfma_f32_16x16x32_{bf16,f16} and v_mfma_f32_16x16x16{bf16_1k,f16}):
-//   lane = 16*q4 + n. Scores: A = keys, row n = token n, lane group q4 supplies 8 dims per
-//   MFMA (dims q4*D/4 + 8*kk .. +8, one contiguous D/4-dim run per lane per tile); B = queries,
-//   column n = head n of the group (zero for n >= G), same dims. The 16x16 result gives lane
-//   (q4, n) the scores of tokens 4*q4 .. 4*q4+3 for head n -- exactly the B operand a 16x16x16
-//   MFMA wants for P^T (k = tokens 4*q4.., column n). Values are stored dim-major in a block, so
-//   the A operand of the value product (row = dim 16*mi + n, k = tokens 4*q4 .. 4*q4+3) is one
-//   contiguous 8-byte (16-bit cache) or 4-byte (fp8) load. No lane shuffles are needed between
-//   the two products; only the running max crosses the four lane groups (two xor shuffles).
+// Operand layouts (v_mfma_f32_16x16x32_{bf16,f16}: lane l = 16*q4 + n holds 8 elements of row
+// n of A and of column n of B, the k-range given by q4; the 16x16 result gives lane (q4, n) rows
+// 4*q4 .. 4*q4+3 of column n):
+//   * scores: A = keys (row n = token n of the block), B = queries (column n = head n of the
+//     group, zero for n >= G); lane group q4 supplies dims dim_base(q4, kk) .. +8 of both, so the
+//     contraction pairs the same dims. The result hands lane (q4, n) the scores of tokens
+//     4*q4 .. 4*q4+3 of the block for head n.
+//   * weighted values over the iteration's two blocks (32 tokens): A = V^T (row = dim
+//     16*mi + n), B = P^T (column = head n); lane group q4 supplies tokens 4*q4 .. 4*q4+3 of
+//     block A then of block B -- exactly the scores it already holds, so no lane shuffles sit
+//     between the two products (only the running max crosses the four lane groups). Values are
+//     stored dim-major in a block, so each lane's piece is one contiguous 8-byte (16-bit) or
+//     4-byte (fp8) load, and one load instruction covers 16 whole 32-byte dim rows.
+//   * keys are staged through LDS with gfx950's direct global -> LDS loads: every load
+//     instruction reads 1 KB of the tile contiguously (whole cache lines, non-temporal) and the
+//     MFMA-layout reads come back out of an XOR-swizzled LDS copy.
 // The weights P are fed to the MFMA as a 16-bit hi part plus a 16-bit remainder (two MFMAs), so
 // they carry ~16 significant bits instead of 8 (bf16) or 11 (fp16).
 // fp8 caches: codes are converted exactly to the MFMA input type; the per-(block, kv head) key
@@ -37,16 +45,6 @@ __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-template <int QDT>
-__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
-  if constexpr (QDT == DT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
 // Two fp32 values that are exactly representable in the 16-bit type -> one packed word.
@@ -69,13 +67,47 @@ __device__ __forceinline__ float from16(uint32_t b) {
   else return f16_bits_to_f32(b);
 }
 
+// First of the 8 contiguous dims lane group q4 contributes to score MFMA kk: 16-bit keys load
+// 16 bytes (8 dims) per MFMA at byte 64*kk + 16*q4 of the row; fp8 keys load 16 bytes (16 dims,
+// two MFMAs) at byte 64*(kk/2) + 16*q4.
+template <int EB>
+__device__ __forceinline__ constexpr int dim_base(int q4, int kk) {
+  return EB == 2 ? 32 * kk + 8 * q4 : 64 * (kk / 2) + 16 * q4 + 8 * (kk % 2);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// gfx950 direct global -> LDS load: each lane's 16 bytes at `src` land at lds_base + 16 * lane.
+template <int AUX>
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_base, 16, 0, AUX);
+}
+
+// Bytes of dynamic LDS the kernel needs: two staged key tiles per wave during the loop, reused
+// by the end-of-work-group merge.
+template <int CDT, int D>
+constexpr size_t mfma_lds_bytes(int G) {
+  const size_t stage = size_t{4} * 2 * 16 * D * Elem<CDT>::bytes;
+  const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
+  return stage > merge ? stage : merge;
+}
+
+// Launch bounds ask for 3 wave64s per SIMD (at most 168 VGPRs + AGPRs per lane): 2 leaves too
+// few tiles in flight per CU, 4 forces spills.
 template <int CDT, int QDT, int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
-  constexpr int KK = D / 32;  // score MFMAs per tile
-  constexpr int MI = D / 16;  // value MFMA tiles (x2 for hi / remainder)
-  constexpr int DQ = D / 4;   // contiguous key dims per lane group
+  constexpr int KK = D / 32;                 // score MFMAs per block
+  constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
+  constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per block
+  constexpr int KT = B * D * EB;             // bytes of one key tile
+  constexpr int CPR = D * EB / 16;           // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;              // key rows per 1 KB load instruction
+  constexpr int NI = B / RPI;                // load instructions per key tile
+  constexpr int kKeyAux = 2;                 // cache policy of the key loads: non-temporal
+  constexpr bool kNtV = true;                // value loads: non-temporal
   extern __shared__ float smem[];
   const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int tid = threadIdx.x;
@@ -100,13 +132,28 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   if (n < G) {
     const u32x4* qp = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const uint8_t*>(a.q) +
-        ((static_cast<size_t>(s) * Hq + g * G + n) * D + q4 * DQ) * 2);
+        ((static_cast<size_t>(s) * Hq + g * G + n) * D) * 2);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qop[kk] = qp[kk];
+    for (int kk = 0; kk < KK; ++kk) qop[kk] = qp[dim_base<EB>(q4, kk) / 8];
   } else {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qop[kk] = u32x4{0u, 0u, 0u, 0u};
   }
+
+  // Key tiles are staged through this wave's two LDS slots. Load instruction ii of a tile covers
+  // 1 KB of it contiguously (rows RPI*ii .. RPI*ii+RPI-1); lane l fetches 16-byte chunk
+  // (l % CPR) ^ (row % CPR) of its row, so LDS holds each row XOR-swizzled by its index and the
+  // score-operand reads below (16 rows at one chunk column) fall into distinct banks.
+  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (2 * KT);
+  int dsrc[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int row = RPI * ii + lane / CPR;
+    dsrc[ii] = row * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
+  }
+  int kread[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) kread[i] = n * CPR * 16 + 16 * ((4 * i + q4) ^ (n % CPR));
 
   f32x4 acc[MI];
 #pragma unroll
@@ -114,89 +161,143 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   float m = neg_inf(), lsum = 0.0f;
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  const size_t tile = static_cast<size_t>(B) * D * EB;
-  for (int j = b0 + wave; j < b1; j += 4) {
-    int pb = trow[j];
-    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
-    const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
-    const uint8_t* kt = a.k_cache + base;
-    const uint8_t* vt = a.v_cache + base;
-    const Raw<DQ * EB> kr = load_raw<DQ * EB>(kt + (n * D + q4 * DQ) * EB);
-    Raw<4 * EB> vr[MI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) vr[mi] = load_raw<4 * EB>(vt + ((16 * mi + n) * B + 4 * q4) * EB);
+  // this wave's blocks are b0 + wave + 4*i, taken two per iteration (blocks A and B); their table
+  // entries are fetched 64 at a time into one VGPR and read back with readlane
+  const int nmine = b0 + wave < b1 ? (b1 - b0 - wave + 3) / 4 : 0;
+  for (int base_i = 0; base_i < nmine; base_i += 64) {
+  const int cnt = min(64, nmine - base_i);
+  int tv = 0;
+  if (lane < cnt) {
+    tv = trow[b0 + wave + 4 * (base_i + lane)];
+    tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
+  }
+  for (int it = 0; it < cnt; it += 2) {
+    const bool two = it + 1 < cnt;
+    const int ja = b0 + wave + 4 * (base_i + it);
+    const int pba = __builtin_amdgcn_readlane(tv, it);
+    const int pbb = two ? __builtin_amdgcn_readlane(tv, it + 1) : pba;
+    const size_t offa = (static_cast<size_t>(pba) * Hkv + g) * KT;
+    const size_t offb = (static_cast<size_t>(pbb) * Hkv + g) * KT;
 
-    float zs = a.zscale, vs = 1.0f;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + offa + dsrc[ii], kbuf + 1024 * ii);
+    if (two) {
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + offb + dsrc[ii], kbuf + KT + 1024 * ii);
+    }
+    Raw<4 * EB> va[MI], vb[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      va[mi] = load_raw<4 * EB, kNtV>(a.v_cache + offa + ((16 * mi + n) * B + 4 * q4) * EB);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      vb[mi] = load_raw<4 * EB, kNtV>(a.v_cache + offb + ((16 * mi + n) * B + 4 * q4) * EB);
+
+    float zsa = a.zscale, zsb = a.zscale, vsa = 1.0f, vsb = 1.0f;
     if constexpr (CDT == DT_FP8) {
-      zs *= a.k_scale[static_cast<size_t>(pb) * Hkv + g];
-      vs = a.v_scale[static_cast<size_t>(pb) * Hkv + g];
+      zsa *= a.k_scale[static_cast<size_t>(pba) * Hkv + g];
+      zsb *= a.k_scale[static_cast<size_t>(pbb) * Hkv + g];
+      vsa = a.v_scale[static_cast<size_t>(pba) * Hkv + g];
+      vsb = a.v_scale[static_cast<size_t>(pbb) * Hkv + g];
     }
+    // The direct-to-LDS loads have landed only once both the vector-memory counter and the LDS
+    // counter have drained (waiting on vmcnt alone let the reads below see stale LDS when the
+    // staged tile was the last one issued), hence the full wait: vmcnt(0) lgkmcnt(0).
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // scores
-    f32x4 zt = f32x4{0.f, 0.f, 0.f, 0.f};
+    // scores of blocks A and B
+    f32x4 zt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 kop;
-      if constexpr (EB == 2) {
-        kop = u32x4{kr.w[4 * kk], kr.w[4 * kk + 1], kr.w[4 * kk + 2], kr.w[4 * kk + 3]};
-      } else {
-        float f[8];
-        to_f32<DT_FP8, 8>(&kr.w[2 * kk], f);
-        kop = u32x4{pack_exact<QDT>(f[0], f[1]), pack_exact<QDT>(f[2], f[3]),
-                    pack_exact<QDT>(f[4], f[5]), pack_exact<QDT>(f[6], f[7])};
+    for (int hb = 0; hb < 2; ++hb) {
+      if (hb == 1 && !two) break;
+      const uint8_t* kb = kbuf + hb * KT;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
+        if constexpr (EB == 2) {
+          zt[hb] = mfma_k32<QDT>(raw, qop[i], zt[hb]);
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t w2[2] = {half ? raw.z : raw.x, half ? raw.w : raw.y};
+            float f[8];
+            to_f32<DT_FP8, 8>(w2, f);
+            const u32x4 kop{pack_exact<QDT>(f[0], f[1]), pack_exact<QDT>(f[2], f[3]),
+                            pack_exact<QDT>(f[4], f[5]), pack_exact<QDT>(f[6], f[7])};
+            zt[hb] = mfma_k32<QDT>(kop, qop[2 * i + half], zt[hb]);
+          }
+        }
       }
-      zt = mfma_k32<QDT>(kop, qop[kk], zt);
     }
-    const int valid = L - j * B - 4 * q4;  // this lane group's tokens below L
-    float z[4];
+    const int valida = L - ja * B - 4 * q4;                    // this lane group's tokens below L
+    const int validb = two ? valida - 4 * B : 0;
+    float z[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = (i < valid) ? zt[i] * zs : neg_inf();
-    float tm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    for (int i = 0; i < 4; ++i) {
+      z[i] = (i < valida) ? zt[0][i] * zsa : neg_inf();
+      z[4 + i] = (i < validb) ? zt[1][i] * zsb : neg_inf();
+    }
+    float tm = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, z[i]);
     tm = fmaxf(tm, __shfl_xor(tm, 16));
     tm = fmaxf(tm, __shfl_xor(tm, 32));
     const float mn = fmaxf(m, tm);  // finite: every block of the sequence holds a valid token
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float pz[4];
+    float pz[8];
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
       psum += pz[i];
     }
     lsum = lsum * alpha + psum;
     m = mn;
 
-    // P^T operand: hi part and remainder
-    uint32_t hb[4], lb[4];
+    // P^T operand over the 32 tokens (k 0..3: block A tokens 4*q4.., k 4..7: block B), as a
+    // 16-bit hi part and remainder
+    uint32_t hbits[8], lbits[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = pz[i] * vs;
-      hb[i] = to16<QDT>(pv);
-      lb[i] = to16<QDT>(pv - from16<QDT>(hb[i]));
+    for (int i = 0; i < 8; ++i) {
+      const float pv = pz[i] * (i < 4 ? vsa : vsb);
+      hbits[i] = to16<QDT>(pv);
+      lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
     }
-    const u32x2 phi = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-    const u32x2 plo = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+    const u32x4 phi{hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16),
+                    hbits[4] | (hbits[5] << 16), hbits[6] | (hbits[7] << 16)};
+    const u32x4 plo{lbits[0] | (lbits[1] << 16), lbits[2] | (lbits[3] << 16),
+                    lbits[4] | (lbits[5] << 16), lbits[6] | (lbits[7] << 16)};
 
     // weighted values; tokens at or beyond L get zero values (their weights are already 0)
-    const uint32_t mk0 = valid >= 2 ? 0xffffffffu : (valid == 1 ? 0x0000ffffu : 0u);
-    const uint32_t mk1 = valid >= 4 ? 0xffffffffu : (valid == 3 ? 0x0000ffffu : 0u);
+    const uint32_t ma0 = valida >= 2 ? 0xffffffffu : (valida == 1 ? 0x0000ffffu : 0u);
+    const uint32_t ma1 = valida >= 4 ? 0xffffffffu : (valida == 3 ? 0x0000ffffu : 0u);
+    const uint32_t mb0 = validb >= 2 ? 0xffffffffu : (validb == 1 ? 0x0000ffffu : 0u);
+    const uint32_t mb1 = validb >= 4 ? 0xffffffffu : (validb == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      u32x2 vop;
+      uint32_t a0, a1, c0, c1;
       if constexpr (EB == 2) {
-        vop = u32x2{vr[mi].w[0], vr[mi].w[1]};
+        a0 = va[mi].w[0];
+        a1 = va[mi].w[1];
+        c0 = vb[mi].w[0];
+        c1 = vb[mi].w[1];
       } else {
         float f[4];
-        to_f32<DT_FP8, 4>(vr[mi].w, f);
-        vop = u32x2{pack_exact<QDT>(f[0], f[1]), pack_exact<QDT>(f[2], f[3])};
+        to_f32<DT_FP8, 4>(va[mi].w, f);
+        a0 = pack_exact<QDT>(f[0], f[1]);
+        a1 = pack_exact<QDT>(f[2], f[3]);
+        to_f32<DT_FP8, 4>(vb[mi].w, f);
+        c0 = pack_exact<QDT>(f[0], f[1]);
+        c1 = pack_exact<QDT>(f[2], f[3]);
       }
-      vop.x &= mk0;
-      vop.y &= mk1;
+      const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
       f32x4 t = acc[mi] * alpha;
-      t = mfma_k16<QDT>(vop, phi, t);
-      acc[mi] = mfma_k16<QDT>(vop, plo, t);
+      t = mfma_k32<QDT>(vop, phi, t);
+      acc[mi] = mfma_k32<QDT>(vop, plo, t);
     }
   }
+  }
+  __syncthreads();  // every wave is done with its staged key tiles: the LDS is reused below
 
   // per-column sum over the four lane groups, then merge the four waves through LDS
   lsum += __shfl_xor(lsum, 16);
@@ -244,9 +345,13 @@ template <int CDT, int QDT>
 static hipError_t launch_mfma_d(const DecodeArgs& a, int D, hipStream_t st) {
   const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
   const int G = a.num_heads / a.num_kv_heads;
-  const size_t shm = (128 + static_cast<size_t>(4) * G * D) * sizeof(float);
-  if (D == 64) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64>), grid, dim3(256), shm, st, a);
-  else if (D == 128) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128>), grid, dim3(256), shm, st, a);
+  if (D == 64) {
+    const size_t shm = mfma_lds_bytes<CDT, 64>(G);
+    hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64>), grid, dim3(256), shm, st, a);
+  } else if (D == 128) {
+    const size_t shm = mfma_lds_bytes<CDT, 128>(G);
+    hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128>), grid, dim3(256), shm, st, a);
+  }
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -68,21 +68,33 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   const size_t tile = static_cast<size_t>(B) * D * EB;  // bytes of one (block, head) tile
-  for (int j = b0 + wave; j < b1; j += 4) {
-    int pb = trow[j];
-    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+  // this wave's blocks are b0 + wave + 4*i; their table entries are fetched 64 at a time into
+  // one VGPR (lane i holds entry i) and read back with readlane, off the per-tile latency chain
+  const int nmine = b0 + wave < b1 ? (b1 - b0 - wave + 3) / 4 : 0;
+  for (int base_i = 0; base_i < nmine; base_i += 64) {
+  const int cnt = min(64, nmine - base_i);
+  int tv = 0;
+  if (lane < cnt) {
+    tv = trow[b0 + wave + 4 * (base_i + lane)];
+    tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
+  }
+  for (int it = 0; it < cnt; ++it) {
+    const int j = b0 + wave + 4 * (base_i + it);
+    const int pb = __builtin_amdgcn_readlane(tv, it);
     const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
     const uint8_t* kt = a.k_cache + base;
     const uint8_t* vt = a.v_cache + base;
 
+    // each key load covers whole token rows (16 lanes x D/16 dims) and each value load whole
+    // dim rows of the block, so full cache lines: streamed non-temporally
     Raw<DPL * EB> kr[TPR];
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
-      kr[i] = load_raw<DPL * EB>(kt + ((r * TPR + i) * D + c * DPL) * EB);
+      kr[i] = load_raw<DPL * EB, true>(kt + ((r * TPR + i) * D + c * DPL) * EB);
     Raw<TPR * EB> vr[DPL];
 #pragma unroll
     for (int jj = 0; jj < DPL; ++jj)
-      vr[jj] = load_raw<TPR * EB>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
+      vr[jj] = load_raw<TPR * EB, true>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
 
     float zs = a.zscale;
     float vs = 1.0f;
@@ -130,6 +142,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       }
     }
   }
+  }
 
   // merge the 16 row states (4 waves x 4 rows) of this work-group
   __shared__ float sm_m[16], sm_l[16];
@@ -167,8 +180,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // One work-group of D threads per (query head, sequence): combines the sequence's partitions.
 // With per-partition maxima m_k, sums l_k and normalised outputs o_k (log2 domain):
 //   out = sum_k w_k o_k / sum_k w_k,   w_k = l_k * exp2(m_k - max_k m_k).
+// The weights are computed once per partition into LDS; every thread then sums over partitions
+// in the same order (deterministic), with the partial-output loads unrolled.
+constexpr int kMergeChunk = 1024;
+
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block_size) {
+  __shared__ float sw[kMergeChunk];
+  __shared__ float sred[D / 64];
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.max_blocks * block_size ? a.max_blocks * block_size : L);
@@ -177,13 +196,30 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
   if (nparts <= 1) return;
   const size_t row = (static_cast<size_t>(s) * a.num_heads + h) * a.max_parts;
   float M = neg_inf();
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws_ml[row + k].x);
+  for (int k = d; k < nparts; k += D) M = fmaxf(M, a.ws_ml[row + k].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((d & 63) == 0) sred[d >> 6] = M;
+  __syncthreads();
+  M = sred[0];
+#pragma unroll
+  for (int i = 1; i < D / 64; ++i) M = fmaxf(M, sred[i]);
   float num = 0.0f, den = 0.0f;
-  for (int k = 0; k < nparts; ++k) {
-    const float2 ml = a.ws_ml[row + k];
-    const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
-    num = __builtin_fmaf(w, a.ws_o[(row + k) * D + d], num);
-    den += w;
+  for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
+    const int n = min(kMergeChunk, nparts - c0);
+    for (int k = d; k < n; k += D) {
+      const float2 ml = a.ws_ml[row + c0 + k];
+      sw[k] = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+    }
+    __syncthreads();
+    const float* po = a.ws_o + (row + c0) * D + d;
+#pragma unroll 8
+    for (int k = 0; k < n; ++k) {
+      const float wk = sw[k];
+      den += wk;
+      num = __builtin_fmaf(wk, po[static_cast<size_t>(k) * D], num);
+    }
+    __syncthreads();
   }
   store_out(a.out, (static_cast<size_t>(s) * a.num_heads + h) * D + d, num / den, a.out_dtype);
 }

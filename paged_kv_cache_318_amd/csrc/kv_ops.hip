@@ -47,36 +47,61 @@ __device__ __forceinline__ float load_as_f32(const void* p, size_t i) {
   else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-// One work-group per new token; threads stride over its num_kv_heads x head_dim elements.
+// One thread per (new token, kv head, 8 consecutive dims): a 16-byte (32-byte for fp32) load of
+// the new key and value, one vector store of the key row piece, and 8 element stores down the
+// dim-major value column. grid = (num_tokens, ceil(Hkv * D / 8 / 256)).
 template <int IN_DT, int C_DT>
-__global__ __launch_bounds__(256) void write_kv_kernel(const void* k_new, const void* v_new,
-                                                       void* k_cache, void* v_cache,
-                                                       const int32_t* slots, int Hkv, int D,
-                                                       int B, int NB, const float* k_scale,
-                                                       const float* v_scale) {
+__global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ k_new,
+                                                       const void* __restrict__ v_new,
+                                                       void* __restrict__ k_cache,
+                                                       void* __restrict__ v_cache,
+                                                       const int32_t* __restrict__ slots, int Hkv,
+                                                       int D, int B, int NB,
+                                                       const float* __restrict__ k_scale,
+                                                       const float* __restrict__ v_scale) {
+  constexpr int IEB = Elem<IN_DT>::bytes;
+  constexpr int CEB = Elem<C_DT>::bytes;
   using CT = typename Store<C_DT>::T;
   const int t = blockIdx.x;
+  const int chunk = blockIdx.y * blockDim.x + threadIdx.x;  // which 8-dim piece of the token
+  const int per_head = D / 8;
+  if (chunk >= Hkv * per_head) return;
   const int slot = slots[t];
   if (slot < 0 || slot >= NB * B) return;  // skipped token (or an out-of-range slot: ignored)
   const int b = slot / B, o = slot - (slot / B) * B;
-  const int n = Hkv * D;
-  CT* kc = reinterpret_cast<CT*>(k_cache);
+  const int hh = chunk / per_head, d0 = (chunk - hh * per_head) * 8;
+  const size_t src = (static_cast<size_t>(t) * Hkv + hh) * D + d0;
+  const Raw<8 * IEB> kr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(k_new) + src * IEB);
+  const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
+  const size_t kdst = ((static_cast<size_t>(b) * Hkv + hh) * B + o) * D + d0;  // elements
+  const size_t vdst = ((static_cast<size_t>(b) * Hkv + hh) * D + d0) * B + o;
+  uint8_t* kc = reinterpret_cast<uint8_t*>(k_cache);
   CT* vc = reinterpret_cast<CT*>(v_cache);
-  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
-    const int hh = idx / D, d = idx - (idx / D) * D;
-    const size_t src = static_cast<size_t>(t) * n + idx;
-    const size_t kdst = ((static_cast<size_t>(b) * Hkv + hh) * B + o) * D + d;
-    const size_t vdst = ((static_cast<size_t>(b) * Hkv + hh) * D + d) * B + o;
-    if constexpr (C_DT == DT_FP8) {
-      const float ks = k_scale[static_cast<size_t>(b) * Hkv + hh];
-      const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
-      const float xk = load_as_f32<IN_DT>(k_new, src);
-      const float xv = load_as_f32<IN_DT>(v_new, src);
-      kc[kdst] = static_cast<CT>(f32_to_e4m3(xk / ks, xk));
-      vc[vdst] = static_cast<CT>(f32_to_e4m3(xv / vs, xv));
-    } else {
-      kc[kdst] = reinterpret_cast<const CT*>(k_new)[src];
-      vc[vdst] = reinterpret_cast<const CT*>(v_new)[src];
+  if constexpr (C_DT == DT_FP8) {
+    const float ks = k_scale[static_cast<size_t>(b) * Hkv + hh];
+    const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
+    float kf[8], vf[8];
+    to_f32<IN_DT, 8>(kr.w, kf);
+    to_f32<IN_DT, 8>(vr.w, vf);
+    uint32_t kw[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kw[e / 4] |= f32_to_e4m3(kf[e] / ks, kf[e]) << (8 * (e & 3));
+      vc[vdst + static_cast<size_t>(e) * B] = static_cast<CT>(f32_to_e4m3(vf[e] / vs, vf[e]));
+    }
+    *reinterpret_cast<u32x2*>(kc + kdst) = u32x2{kw[0], kw[1]};
+  } else {
+    static_assert(IN_DT == C_DT, "a 16/32-bit cache stores the input bits");
+#pragma unroll
+    for (int i = 0; i < 8 * CEB / 16; ++i)
+      reinterpret_cast<u32x4*>(kc + kdst * CEB)[i] =
+          u32x4{kr.w[4 * i], kr.w[4 * i + 1], kr.w[4 * i + 2], kr.w[4 * i + 3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      CT v;
+      if constexpr (CEB == 4) v = vr.w[e];
+      else v = static_cast<CT>(vr.w[e / 2] >> (16 * (e & 1)));
+      vc[vdst + static_cast<size_t>(e) * B] = v;
     }
   }
 }
@@ -139,7 +164,8 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
                            const int32_t* slots, int T, int Hkv, int D, int B, int NB, int in_dt,
                            int cache_dt, const float* k_scale, const float* v_scale,
                            hipStream_t st) {
-  const dim3 grid(T), block(256);
+  const int chunks = Hkv * (D / 8);
+  const dim3 grid(T, (chunks + 255) / 256), block(256);
 #define PA_WRITE(I, C)                                                                         \
   hipLaunchKernelGGL((write_kv_kernel<I, C>), grid, block, 0, st, k_new, v_new, k_cache,       \
                      v_cache, slots, Hkv, D, B, NB, k_scale, v_scale)

@@ -15,7 +15,12 @@
 
 namespace {
 
-constexpr int kDefaultPartitionTokens = 512;
+// Default partition lengths (tokens), from sweeps of 128..1024 on the decode workloads: the
+// VALU kernel (one query head per work-group) is best at 512, the MFMA kernel (a whole query
+// group per work-group, fewer and heavier work-groups) at 1024. Workspaces are sized for the
+// shorter one, so they fit either.
+constexpr int kDefaultPartitionValu = 512;
+constexpr int kDefaultPartitionMfma = 1024;
 constexpr int kMaxGridYZ = 65535;
 
 bool dtype_ok(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
@@ -65,8 +70,10 @@ struct Plan {
   int part_blocks;
   int max_parts;
 };
-Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens) {
-  const int pt = partition_tokens > 0 ? partition_tokens : kDefaultPartitionTokens;
+Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens,
+                     bool mfma = false) {
+  const int pt = partition_tokens > 0 ? partition_tokens
+                                      : (mfma ? kDefaultPartitionMfma : kDefaultPartitionValu);
   int pb = pt / block_size;
   if (pb < 1) pb = 1;
   return Plan{pb, (max_blocks_per_seq + pb - 1) / pb};
@@ -211,7 +218,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   } else {
     use_mfma = mfma_ok && G >= 2;
   }
-  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens);
+  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma);
   if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   const size_t need = workspace_for(num_seqs, num_heads, head_dim, pl);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;

@@ -33,22 +33,29 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // 16-aligned for NB >= 16) by construction of the layouts -------------------------------------
 template <int NB> struct Raw { uint32_t w[NB >= 4 ? NB / 4 : 1]; };
 
-template <int NB>
+// NT = true marks the load non-temporal (streamed through the caches, allocated for eviction
+// first): used for K/V tiles, which are read exactly once per call, when every load instruction
+// of a wave covers whole 128-byte lines.
+template <int NB, bool NT = false>
 __device__ __forceinline__ Raw<NB> load_raw(const void* p) {
   Raw<NB> r;
   if constexpr (NB == 2) {
-    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+    r.w[0] = NT ? __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))
+                : *reinterpret_cast<const uint16_t*>(p);
   } else if constexpr (NB == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p))
+                : *reinterpret_cast<const uint32_t*>(p);
   } else if constexpr (NB == 8) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    u32x2 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                 : *reinterpret_cast<const u32x2*>(p);
     r.w[0] = v.x;
     r.w[1] = v.y;
   } else {
     static_assert(NB % 16 == 0, "unsupported load width");
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i) {
-      u32x4 v = reinterpret_cast<const u32x4*>(p)[i];
+      u32x4 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i)
+                   : reinterpret_cast<const u32x4*>(p)[i];
       r.w[4 * i + 0] = v.x;
       r.w[4 * i + 1] = v.y;
       r.w[4 * i + 2] = v.z;

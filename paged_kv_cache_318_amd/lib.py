@@ -19,7 +19,8 @@ PA_KERNEL_DECODE_PARTITION, PA_KERNEL_DECODE_MERGE, PA_KERNEL_WRITE_KV, PA_KERNE
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
           -4: "PA_ERR_HIP"}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -35,6 +36,7 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                    _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_diag_read_bandwidth": ([_vp, _sz, _vp, _i32, _i32, _vp, _vp], _i32),
     "pa_profile_enable": ([_i32], _i32),
     "pa_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)],
                         _i32),
@@ -172,6 +174,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         S, Hq, Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
         _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def pa_diag_read_bandwidth(buf, tile_bytes: int, num_tiles: int, tile_order=None, sink=None,
+                           stream=None) -> None:
+    """Diagnostic read of ``num_tiles`` tiles of ``buf`` (a GPU tensor), in address order or in
+    the order of the int32 tensor ``tile_order``."""
+    import torch
+    if sink is None:
+        sink = torch.empty(64 * 1024, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check("pa_diag_read_bandwidth", load().pa_diag_read_bandwidth(
+        _ptr(buf), nbytes // tile_bytes, _ptr(tile_order), int(num_tiles), int(tile_bytes),
+        _ptr(sink), _stream(stream)))
 
 
 def pa_profile_enable(on: bool = True) -> None:
