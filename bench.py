@@ -162,6 +162,12 @@ def main():
           f"{w.kv_bytes() / 1e9:.3f} GB K/V per call, generated in {t_gen:.1f}s", file=sys.stderr,
           flush=True)
 
+    # the host knows from its tables whether sequences share physical blocks; if so, pa_decode is
+    # told to read K/V through the caches
+    import numpy as np
+    used = np.concatenate([w.tables[s, : -(-int(L) // w.block_size)] for s, L in enumerate(w.lens)])
+    shared = bool(used.size) and np.unique(used).size < used.size
+    flags = lib.PA_DECODE_SHARED_BLOCKS if shared else 0
     reps = [upload(w) for _ in range(max(1, args.replicas))]
     out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(w.q_dtype), device="cuda")
     ws = workspace_for(reps[0].q, reps[0].tables, w.block_size, args.partition)
@@ -170,7 +176,7 @@ def main():
         d = reps[i % len(reps)]
         decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
-                    variant=args.variant, workspace=ws)
+                    variant=args.variant, workspace=ws, flags=flags)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20)
@@ -242,7 +248,8 @@ def main():
             "attended_tokens": w.attended_tokens, "num_blocks": w.num_blocks,
             "cow_pairs": int(w.cow.shape[0]), "step_bytes": step_bytes,
             "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
-            "replicas": len(reps), "partition_tokens": args.partition, "variant": args.variant,
+            "replicas": args.replicas, "partition_tokens": args.partition, "variant": args.variant,
+            "shared_blocks_flag": shared,
         },
         "kernels_us": {
             "step_with_events": round(1e3 * ms_step_profiled, 2),

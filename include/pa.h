@@ -70,6 +70,9 @@ typedef enum {
   PA_VARIANT_MFMA = 2  /* one work-group per kv head: the query group x block on MFMA        */
 } pa_variant;
 
+/* pa_decode flags. */
+enum { PA_DECODE_SHARED_BLOCKS = 1 };
+
 /* Human-readable name of a pa_status value (static string, never NULL). */
 const char* pa_status_string(int status);
 
@@ -151,6 +154,10 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
  *   num_heads % num_kv_heads == 0; head_dim in {64, 128}; block_size in {8, 16, 32}.
  *   variant: pa_variant; PA_VARIANT_MFMA needs a 16-bit or fp8 cache, block_size 16 and at most
  *   16 query heads per kv head.
+ *   flags: 0 or PA_DECODE_SHARED_BLOCKS (a hint, never a change of result): several sequences of
+ *   the batch reference the same physical blocks (shared prefixes, parallel samples), so K/V are
+ *   read through the caches and a shared block fetched for one sequence is reused by the others.
+ *   Without it K/V are streamed non-temporally, which is faster when every block is read once.
  *   workspace: device memory of at least pa_decode_workspace_bytes(...) bytes (may be NULL when
  *   that is 0). Results are deterministic: the same inputs give the same bits, whatever the
  *   physical placement of the blocks.
@@ -160,8 +167,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
               pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
-              const float* v_scale, int partition_tokens, int variant, void* workspace,
-              size_t workspace_bytes, void* stream);
+              const float* v_scale, int partition_tokens, int variant, int flags,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Profiling: when enabled, every pa_* launch is bracketed by HIP events on its stream.

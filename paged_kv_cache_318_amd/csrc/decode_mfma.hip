@@ -47,13 +47,15 @@ __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Two fp32 values that are exactly representable in the 16-bit type -> one packed word.
-template <int QDT>
-__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+// Two OCP E4M3 codes (bytes 0-1 of `w`, or 2-3 when HI) -> two packed 16-bit values of the
+// MFMA input type, with gfx950's scaled converter at scale 1.0: one instruction, exact (every
+// E4M3 value is representable in bf16 and fp16).
+template <int QDT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to16(uint32_t w) {
   if constexpr (QDT == DT_BF16)
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   else
-    return f32_to_f16_rne(lo) | (f32_to_f16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
 template <int QDT>
@@ -84,18 +86,26 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_base, 16, 0, AUX);
 }
 
-// Bytes of dynamic LDS the kernel needs: two staged key tiles per wave during the loop, reused
+// Blocks a wave takes per iteration: two (16 KB of K/V in flight per wave at 16 bits, 8 KB for
+// fp8; four fp8 blocks per iteration measured slower).
+constexpr int kFp8BlocksPerIter = 2;
+constexpr int mfma_blocks_per_iter(int elem_bytes) { return elem_bytes == 2 ? 2 : kFp8BlocksPerIter; }
+
+// Bytes of dynamic LDS the kernel needs: the staged key tiles of one iteration per wave, reused
 // by the end-of-work-group merge.
 template <int CDT, int D>
 constexpr size_t mfma_lds_bytes(int G) {
-  const size_t stage = size_t{4} * 2 * 16 * D * Elem<CDT>::bytes;
+  const size_t stage =
+      size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes;
   const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
   return stage > merge ? stage : merge;
 }
 
 // Launch bounds ask for 3 wave64s per SIMD (at most 168 VGPRs + AGPRs per lane): 2 leaves too
 // few tiles in flight per CU, 4 forces spills.
-template <int CDT, int QDT, int D>
+// NT: non-temporal K/V loads (streaming; the default) or cached ones (blocks shared between
+// sequences of the batch).
+template <int CDT, int QDT, int D, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
@@ -106,8 +116,9 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int CPR = D * EB / 16;           // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;              // key rows per 1 KB load instruction
   constexpr int NI = B / RPI;                // load instructions per key tile
-  constexpr int kKeyAux = 2;                 // cache policy of the key loads: non-temporal
-  constexpr bool kNtV = true;                // value loads: non-temporal
+  constexpr int NBI = mfma_blocks_per_iter(EB);  // blocks per iteration (16 KB in flight)
+  constexpr int kKeyAux = NT ? 2 : 0;        // cache policy of the key loads (2: non-temporal)
+  constexpr bool kNtV = NT;
   extern __shared__ float smem[];
   const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int tid = threadIdx.x;
@@ -140,11 +151,11 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     for (int kk = 0; kk < KK; ++kk) qop[kk] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Key tiles are staged through this wave's two LDS slots. Load instruction ii of a tile covers
+  // Key tiles are staged through this wave's NBI LDS slots. Load instruction ii of a tile covers
   // 1 KB of it contiguously (rows RPI*ii .. RPI*ii+RPI-1); lane l fetches 16-byte chunk
   // (l % CPR) ^ (row % CPR) of its row, so LDS holds each row XOR-swizzled by its index and the
   // score-operand reads below (16 rows at one chunk column) fall into distinct banks.
-  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (2 * KT);
+  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT);
   int dsrc[NI];
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
@@ -161,8 +172,8 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   float m = neg_inf(), lsum = 0.0f;
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  // this wave's blocks are b0 + wave + 4*i, taken two per iteration (blocks A and B); their table
-  // entries are fetched 64 at a time into one VGPR and read back with readlane
+  // this wave's blocks are b0 + wave + 4*i, taken NBI per iteration; their table entries are
+  // fetched 64 at a time into one VGPR and read back with readlane
   const int nmine = b0 + wave < b1 ? (b1 - b0 - wave + 3) / 4 : 0;
   for (int base_i = 0; base_i < nmine; base_i += 64) {
   const int cnt = min(64, nmine - base_i);
@@ -171,129 +182,134 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
     tv = trow[b0 + wave + 4 * (base_i + lane)];
     tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
   }
-  for (int it = 0; it < cnt; it += 2) {
-    const bool two = it + 1 < cnt;
+  for (int it = 0; it < cnt; it += NBI) {
+    const int nlive = min(NBI, cnt - it);  // blocks of this iteration (the last may have fewer)
     const int ja = b0 + wave + 4 * (base_i + it);
-    const int pba = __builtin_amdgcn_readlane(tv, it);
-    const int pbb = two ? __builtin_amdgcn_readlane(tv, it + 1) : pba;
-    const size_t offa = (static_cast<size_t>(pba) * Hkv + g) * KT;
-    const size_t offb = (static_cast<size_t>(pbb) * Hkv + g) * KT;
-
+    int pbs[NBI];
+    size_t offs[NBI];
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + offa + dsrc[ii], kbuf + 1024 * ii);
-    if (two) {
-#pragma unroll
-      for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + offb + dsrc[ii], kbuf + KT + 1024 * ii);
+    for (int u = 0; u < NBI; ++u) {
+      pbs[u] = __builtin_amdgcn_readlane(tv, it + (u < nlive ? u : 0));
+      offs[u] = (static_cast<size_t>(pbs[u]) * Hkv + g) * KT;
     }
-    Raw<4 * EB> va[MI], vb[MI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      va[mi] = load_raw<4 * EB, kNtV>(a.v_cache + offa + ((16 * mi + n) * B + 4 * q4) * EB);
+    for (int u = 0; u < NBI; ++u) {
+      if (u >= nlive) break;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      vb[mi] = load_raw<4 * EB, kNtV>(a.v_cache + offb + ((16 * mi + n) * B + 4 * q4) * EB);
+      for (int ii = 0; ii < NI; ++ii)
+        dma16<kKeyAux>(a.k_cache + offs[u] + dsrc[ii], kbuf + u * KT + 1024 * ii);
+    }
+    Raw<4 * EB> vr[NBI][MI];
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + offs[u] + ((16 * mi + n) * B + 4 * q4) * EB);
 
-    float zsa = a.zscale, zsb = a.zscale, vsa = 1.0f, vsb = 1.0f;
-    if constexpr (CDT == DT_FP8) {
-      zsa *= a.k_scale[static_cast<size_t>(pba) * Hkv + g];
-      zsb *= a.k_scale[static_cast<size_t>(pbb) * Hkv + g];
-      vsa = a.v_scale[static_cast<size_t>(pba) * Hkv + g];
-      vsb = a.v_scale[static_cast<size_t>(pbb) * Hkv + g];
+    float zs[NBI], vs[NBI];
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {
+      zs[u] = a.zscale;
+      vs[u] = 1.0f;
+      if constexpr (CDT == DT_FP8) {
+        zs[u] *= a.k_scale[static_cast<size_t>(pbs[u]) * Hkv + g];
+        vs[u] = a.v_scale[static_cast<size_t>(pbs[u]) * Hkv + g];
+      }
     }
     // The direct-to-LDS loads have landed only once both the vector-memory counter and the LDS
     // counter have drained (waiting on vmcnt alone let the reads below see stale LDS when the
     // staged tile was the last one issued), hence the full wait: vmcnt(0) lgkmcnt(0).
     __builtin_amdgcn_s_waitcnt(0);
 
-    // scores of blocks A and B
-    f32x4 zt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // scores of the iteration's blocks
+    f32x4 zt[NBI];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      if (hb == 1 && !two) break;
-      const uint8_t* kb = kbuf + hb * KT;
+    for (int u = 0; u < NBI; ++u) {
+      zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u >= nlive) continue;
+      const uint8_t* kb = kbuf + u * KT;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
         if constexpr (EB == 2) {
-          zt[hb] = mfma_k32<QDT>(raw, qop[i], zt[hb]);
+          zt[u] = mfma_k32<QDT>(raw, qop[i], zt[u]);
         } else {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const uint32_t w2[2] = {half ? raw.z : raw.x, half ? raw.w : raw.y};
-            float f[8];
-            to_f32<DT_FP8, 8>(w2, f);
-            const u32x4 kop{pack_exact<QDT>(f[0], f[1]), pack_exact<QDT>(f[2], f[3]),
-                            pack_exact<QDT>(f[4], f[5]), pack_exact<QDT>(f[6], f[7])};
-            zt[hb] = mfma_k32<QDT>(kop, qop[2 * i + half], zt[hb]);
-          }
+          const u32x4 k0{fp8x2_to16<QDT, false>(raw.x), fp8x2_to16<QDT, true>(raw.x),
+                         fp8x2_to16<QDT, false>(raw.y), fp8x2_to16<QDT, true>(raw.y)};
+          zt[u] = mfma_k32<QDT>(k0, qop[2 * i], zt[u]);
+          const u32x4 k1{fp8x2_to16<QDT, false>(raw.z), fp8x2_to16<QDT, true>(raw.z),
+                         fp8x2_to16<QDT, false>(raw.w), fp8x2_to16<QDT, true>(raw.w)};
+          zt[u] = mfma_k32<QDT>(k1, qop[2 * i + 1], zt[u]);
         }
       }
     }
-    const int valida = L - ja * B - 4 * q4;                    // this lane group's tokens below L
-    const int validb = two ? valida - 4 * B : 0;
-    float z[8];
+    int valid[NBI];  // this lane group's tokens below L, per block (<= 0: none)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = (i < valida) ? zt[0][i] * zsa : neg_inf();
-      z[4 + i] = (i < validb) ? zt[1][i] * zsb : neg_inf();
-    }
+    for (int u = 0; u < NBI; ++u) valid[u] = u < nlive ? L - (ja + 4 * u) * B - 4 * q4 : 0;
+    float z[4 * NBI];
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[4 * u + i] = (i < valid[u]) ? zt[u][i] * zs[u] : neg_inf();
     float tm = z[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, z[i]);
+    for (int i = 1; i < 4 * NBI; ++i) tm = fmaxf(tm, z[i]);
     tm = fmaxf(tm, __shfl_xor(tm, 16));
     tm = fmaxf(tm, __shfl_xor(tm, 32));
     const float mn = fmaxf(m, tm);  // finite: every block of the sequence holds a valid token
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float pz[8];
+    float pz[4 * NBI];
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 * NBI; ++i) {
       pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
       psum += pz[i];
     }
     lsum = lsum * alpha + psum;
     m = mn;
-
-    // P^T operand over the 32 tokens (k 0..3: block A tokens 4*q4.., k 4..7: block B), as a
-    // 16-bit hi part and remainder
-    uint32_t hbits[8], lbits[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pv = pz[i] * (i < 4 ? vsa : vsb);
-      hbits[i] = to16<QDT>(pv);
-      lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
-    }
-    const u32x4 phi{hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16),
-                    hbits[4] | (hbits[5] << 16), hbits[6] | (hbits[7] << 16)};
-    const u32x4 plo{lbits[0] | (lbits[1] << 16), lbits[2] | (lbits[3] << 16),
-                    lbits[4] | (lbits[5] << 16), lbits[6] | (lbits[7] << 16)};
+    for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
 
-    // weighted values; tokens at or beyond L get zero values (their weights are already 0)
-    const uint32_t ma0 = valida >= 2 ? 0xffffffffu : (valida == 1 ? 0x0000ffffu : 0u);
-    const uint32_t ma1 = valida >= 4 ? 0xffffffffu : (valida == 3 ? 0x0000ffffu : 0u);
-    const uint32_t mb0 = validb >= 2 ? 0xffffffffu : (validb == 1 ? 0x0000ffffu : 0u);
-    const uint32_t mb1 = validb >= 4 ? 0xffffffffu : (validb == 3 ? 0x0000ffffu : 0u);
+    // weighted values, two blocks (32 tokens) per MFMA: k 0..3 are tokens 4*q4.. of the pair's
+    // first block, k 4..7 those of its second; P^T goes in as a 16-bit hi part and remainder.
+    // Tokens at or beyond L get zero values (their weights are already 0).
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      uint32_t a0, a1, c0, c1;
-      if constexpr (EB == 2) {
-        a0 = va[mi].w[0];
-        a1 = va[mi].w[1];
-        c0 = vb[mi].w[0];
-        c1 = vb[mi].w[1];
-      } else {
-        float f[4];
-        to_f32<DT_FP8, 4>(va[mi].w, f);
-        a0 = pack_exact<QDT>(f[0], f[1]);
-        a1 = pack_exact<QDT>(f[2], f[3]);
-        to_f32<DT_FP8, 4>(vb[mi].w, f);
-        c0 = pack_exact<QDT>(f[0], f[1]);
-        c1 = pack_exact<QDT>(f[2], f[3]);
+    for (int pr = 0; pr < NBI / 2; ++pr) {
+      if (2 * pr >= nlive) break;
+      const int u0 = 2 * pr, u1 = 2 * pr + 1;
+      uint32_t hbits[8], lbits[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = pz[4 * u0 + i] * (i < 4 ? vs[u0] : vs[u1]);
+        hbits[i] = to16<QDT>(pv);
+        lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
       }
-      const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
-      f32x4 t = acc[mi] * alpha;
-      t = mfma_k32<QDT>(vop, phi, t);
-      acc[mi] = mfma_k32<QDT>(vop, plo, t);
+      const u32x4 phi{hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16),
+                      hbits[4] | (hbits[5] << 16), hbits[6] | (hbits[7] << 16)};
+      const u32x4 plo{lbits[0] | (lbits[1] << 16), lbits[2] | (lbits[3] << 16),
+                      lbits[4] | (lbits[5] << 16), lbits[6] | (lbits[7] << 16)};
+      const uint32_t ma0 = valid[u0] >= 2 ? 0xffffffffu : (valid[u0] == 1 ? 0x0000ffffu : 0u);
+      const uint32_t ma1 = valid[u0] >= 4 ? 0xffffffffu : (valid[u0] == 3 ? 0x0000ffffu : 0u);
+      const uint32_t mb0 = valid[u1] >= 2 ? 0xffffffffu : (valid[u1] == 1 ? 0x0000ffffu : 0u);
+      const uint32_t mb1 = valid[u1] >= 4 ? 0xffffffffu : (valid[u1] == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        uint32_t a0, a1, c0, c1;
+        if constexpr (EB == 2) {
+          a0 = vr[u0][mi].w[0];
+          a1 = vr[u0][mi].w[1];
+          c0 = vr[u1][mi].w[0];
+          c1 = vr[u1][mi].w[1];
+        } else {
+          a0 = fp8x2_to16<QDT, false>(vr[u0][mi].w[0]);
+          a1 = fp8x2_to16<QDT, true>(vr[u0][mi].w[0]);
+          c0 = fp8x2_to16<QDT, false>(vr[u1][mi].w[0]);
+          c1 = fp8x2_to16<QDT, true>(vr[u1][mi].w[0]);
+        }
+        const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
+        acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
+        acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
+      }
     }
   }
   }
@@ -347,10 +363,12 @@ static hipError_t launch_mfma_d(const DecodeArgs& a, int D, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
   if (D == 64) {
     const size_t shm = mfma_lds_bytes<CDT, 64>(G);
-    hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64, false>), grid, dim3(256), shm, st, a);
   } else if (D == 128) {
     const size_t shm = mfma_lds_bytes<CDT, 128>(G);
-    hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128, false>), grid, dim3(256), shm, st, a);
   }
   else return hipErrorInvalidValue;
   return hipGetLastError();

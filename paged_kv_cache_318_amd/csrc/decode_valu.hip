@@ -28,7 +28,12 @@
 
 namespace pa {
 
-template <int CDT, int QDT, int D, int B>
+// Blocks whose loads a wave issues together before their math (tiles in flight per wave).
+constexpr int kValuBlocksPerIter = 2;
+
+// NT: read K/V tiles non-temporally (streaming; the default) or through the caches (when blocks
+// are shared between sequences of the batch and a tile fetched for one is reused by another).
+template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int QB = Elem<QDT>::bytes;
@@ -78,24 +83,33 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     tv = trow[b0 + wave + 4 * (base_i + lane)];
     tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
   }
-  for (int it = 0; it < cnt; ++it) {
-    const int j = b0 + wave + 4 * (base_i + it);
-    const int pb = __builtin_amdgcn_readlane(tv, it);
-    const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
-    const uint8_t* kt = a.k_cache + base;
-    const uint8_t* vt = a.v_cache + base;
-
-    // each key load covers whole token rows (16 lanes x D/16 dims) and each value load whole
-    // dim rows of the block, so full cache lines: streamed non-temporally
-    Raw<DPL * EB> kr[TPR];
+  for (int it = 0; it < cnt; it += kValuBlocksPerIter) {
+    // issue the loads of up to kValuBlocksPerIter blocks before any of their math, so each wave
+    // keeps that many tiles in flight
+    Raw<DPL * EB> kr[kValuBlocksPerIter][TPR];
+    Raw<TPR * EB> vr[kValuBlocksPerIter][DPL];
+    int pbs[kValuBlocksPerIter];
 #pragma unroll
-    for (int i = 0; i < TPR; ++i)
-      kr[i] = load_raw<DPL * EB, true>(kt + ((r * TPR + i) * D + c * DPL) * EB);
-    Raw<TPR * EB> vr[DPL];
+    for (int u = 0; u < kValuBlocksPerIter; ++u) {
+      if (it + u >= cnt) break;
+      pbs[u] = __builtin_amdgcn_readlane(tv, it + u);
+      const size_t base = (static_cast<size_t>(pbs[u]) * Hkv + g) * tile;
+      const uint8_t* kt = a.k_cache + base;
+      const uint8_t* vt = a.v_cache + base;
+      // each key load covers whole token rows (16 lanes x D/16 dims) and each value load whole
+      // dim rows of the block, so full cache lines
 #pragma unroll
-    for (int jj = 0; jj < DPL; ++jj)
-      vr[jj] = load_raw<TPR * EB, true>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
-
+      for (int i = 0; i < TPR; ++i)
+        kr[u][i] = load_raw<DPL * EB, NT>(kt + ((r * TPR + i) * D + c * DPL) * EB);
+#pragma unroll
+      for (int jj = 0; jj < DPL; ++jj)
+        vr[u][jj] = load_raw<TPR * EB, NT>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
+    }
+#pragma unroll
+    for (int u = 0; u < kValuBlocksPerIter; ++u) {
+    if (it + u >= cnt) break;
+    const int j = b0 + wave + 4 * (base_i + it + u);
+    const int pb = pbs[u];
     float zs = a.zscale;
     float vs = 1.0f;
     if constexpr (CDT == DT_FP8) {
@@ -108,7 +122,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < TPR; ++i) {
       float kf[DPL];
-      to_f32<CDT, DPL>(kr[i].w, kf);
+      to_f32<CDT, DPL>(kr[u][i].w, kf);
       float dot = 0.0f;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
@@ -133,13 +147,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj) {
         float vf[TPR];
-        to_f32<CDT, TPR>(vr[jj].w, vf);
+        to_f32<CDT, TPR>(vr[u][jj].w, vf);
         float t = acc[jj] * alpha;
         float pv = 0.0f;
 #pragma unroll
         for (int i = 0; i < TPR; ++i) pv = __builtin_fmaf(pz[i], (i < valid) ? vf[i] : 0.0f, pv);
         acc[jj] = __builtin_fmaf(pv, vs, t);
       }
+    }
     }
   }
   }
@@ -225,12 +240,18 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
 }
 
 // ---- launchers ----------------------------------------------------------------------------------
+template <int CDT, int QDT, int D, int B>
+static void launch_valu_nt(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (a.stream_kv) hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, false>), grid, dim3(256), 0, st, a);
+}
+
 template <int CDT, int QDT, int D>
 static hipError_t launch_valu_b(const DecodeArgs& a, int B, dim3 grid, hipStream_t st) {
   switch (B) {
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 8>), grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 16>), grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, 32>), grid, dim3(256), 0, st, a); break;
+    case 8: launch_valu_nt<CDT, QDT, D, 8>(a, grid, st); break;
+    case 16: launch_valu_nt<CDT, QDT, D, 16>(a, grid, st); break;
+    case 32: launch_valu_nt<CDT, QDT, D, 32>(a, grid, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -15,12 +15,16 @@
 
 namespace {
 
-// Default partition lengths (tokens), from sweeps of 128..1024 on the decode workloads: the
-// VALU kernel (one query head per work-group) is best at 512, the MFMA kernel (a whole query
-// group per work-group, fewer and heavier work-groups) at 1024. Workspaces are sized for the
-// shorter one, so they fit either.
+// Default partition lengths (tokens), from sweeps of 128..8192 on the decode workloads. The
+// VALU kernel (one query head per work-group) is best at 512. The MFMA kernel (a whole query
+// group per work-group: fewer, heavier work-groups, each paying a few microseconds to fetch its
+// length, table entries and first tiles) is best at 1024 when there are many (sequence, kv head)
+// units to spread over the CUs, and at 2048 when there are few (long sequences, split more).
+// Workspaces are sized for the shortest default, so they fit every choice.
 constexpr int kDefaultPartitionValu = 512;
 constexpr int kDefaultPartitionMfma = 1024;
+constexpr int kDefaultPartitionMfmaFewUnits = 2048;
+constexpr int kFewUnits = 256;
 constexpr int kMaxGridYZ = 65535;
 
 bool dtype_ok(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
@@ -71,9 +75,12 @@ struct Plan {
   int max_parts;
 };
 Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens,
-                     bool mfma = false) {
-  const int pt = partition_tokens > 0 ? partition_tokens
-                                      : (mfma ? kDefaultPartitionMfma : kDefaultPartitionValu);
+                     bool mfma = false, long long units = 0) {
+  int pt = partition_tokens;
+  if (pt <= 0) {
+    pt = !mfma ? kDefaultPartitionValu
+               : (units >= kFewUnits ? kDefaultPartitionMfma : kDefaultPartitionMfmaFewUnits);
+  }
   int pb = pt / block_size;
   if (pb < 1) pb = 1;
   return Plan{pb, (max_blocks_per_seq + pb - 1) / pb};
@@ -187,8 +194,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
               pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
-              const float* v_scale, int partition_tokens, int variant, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              const float* v_scale, int partition_tokens, int variant, int flags,
+              void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
@@ -196,6 +203,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
   if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_INVALID_ARG;
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
     return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
@@ -218,7 +226,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   } else {
     use_mfma = mfma_ok && G >= 2;
   }
-  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma);
+  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma,
+                                  static_cast<long long>(num_seqs) * num_kv_heads);
   if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   const size_t need = workspace_for(num_seqs, num_heads, head_dim, pl);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
@@ -246,6 +255,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.max_parts = pl.max_parts;
   a.out_dtype = out_dtype;
   a.zscale = scale * pa::kLog2e;
+  a.stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) ? 0 : 1;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;

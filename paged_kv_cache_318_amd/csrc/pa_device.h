@@ -152,6 +152,7 @@ struct DecodeArgs {
   float2* ws_ml;   // [S][Hq][max_parts] = (max of log2-scaled scores, sum of exp2)
   int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks;
   int part_blocks, max_parts, out_dtype;
+  int stream_kv;   // 1: K/V read non-temporally; 0: through the caches (shared blocks)
   float zscale;    // softmax scale * log2(e)
 };
 

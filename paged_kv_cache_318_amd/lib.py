@@ -14,6 +14,7 @@ from typing import Optional
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+PA_DECODE_SHARED_BLOCKS = 1
 PA_KERNEL_DECODE_PARTITION, PA_KERNEL_DECODE_MERGE, PA_KERNEL_WRITE_KV, PA_KERNEL_COPY_BLOCKS, \
     PA_KERNEL_GATHER_KV = range(5)
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
@@ -35,7 +36,7 @@ _SIGS = {
                       _vp], _i32),
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                   _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
+                   _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_diag_read_bandwidth": ([_vp, _sz, _vp, _i32, _i32, _vp, _vp], _i32),
     "pa_profile_enable": ([_i32], _i32),
     "pa_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)],
@@ -156,7 +157,7 @@ def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale=None,
               v_scale=None, partition_tokens: int = 0, variant: int = PA_VARIANT_AUTO,
-              workspace=None, stream=None) -> None:
+              workspace=None, stream=None, flags: int = 0) -> None:
     """out/q [S][Hq][D]; caches as in pa_write_kv; block_tables int32 [S][MB]; lens int32 [S].
     ``workspace``: a uint8 GPU tensor of at least ``pa_decode_workspace_bytes`` bytes."""
     import torch
@@ -172,8 +173,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
     _check("pa_decode", load().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         S, Hq, Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
-        _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), int(flags),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def pa_diag_read_bandwidth(buf, tile_bytes: int, num_tiles: int, tile_order=None, sink=None,

@@ -74,17 +74,19 @@ def test_workspace_bytes(L):
 def _decode(L, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, S=4, Hq=8, Hkv=2, D=128, B=16,
              MB=8, NB=64, scale=0.125, qdt=BF16, cdt=BF16, odt=BF16, ks=None, vs=None, part=0,
-             variant=0, ws=None, wsb=0)
+             variant=0, flags=0, ws=None, wsb=0)
     a.update(kw)
     return L.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["S"], a["Hq"],
                        a["Hkv"], a["D"], a["B"], a["MB"], a["NB"], a["scale"], a["qdt"], a["cdt"],
-                       a["odt"], a["ks"], a["vs"], a["part"], a["variant"], a["ws"], a["wsb"], None)
+                       a["odt"], a["ks"], a["vs"], a["part"], a["variant"], a["flags"], a["ws"],
+                       a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(S=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=3), INVALID), (dict(NB=0), INVALID),
     (dict(MB=0), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(qdt=7), INVALID), (dict(variant=5), INVALID), (dict(part=24), INVALID),
+    (dict(flags=2), INVALID), (dict(flags=-1), INVALID),
     (dict(part=-16), INVALID), (dict(NB=1 << 28), INVALID), (dict(out=None), INVALID),
     (dict(tab=None), INVALID), (dict(D=96), UNSUPPORTED), (dict(B=4), UNSUPPORTED),
     (dict(qdt=F16, cdt=BF16, odt=F16), UNSUPPORTED), (dict(qdt=F32, cdt=FP8, odt=F32), UNSUPPORTED),

@@ -77,14 +77,15 @@ def _check_inputs(w):
     assert np.all((w.cow >= 0) & (w.cow < NB))
 
 
-def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False):
+def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False, flags=0):
     _check_inputs(w)
     d = upload(w)
     out_dt = out_dt or w.q_dtype
     out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(out_dt), device="cuda")
     ws = workspace_for(d.q, d.tables, w.block_size, part)
     decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
-                w.scale, d.k_scale, d.v_scale, partition_tokens=part, variant=variant, workspace=ws)
+                w.scale, d.k_scale, d.v_scale, partition_tokens=part, variant=variant, workspace=ws,
+                flags=flags)
     torch.cuda.synchronize()
     res = to_numpy_f64(out)
     if return_pools:
@@ -147,11 +148,13 @@ def test_config4_shared_prefix(first_step):
     w = cfg(4, first_step=first_step)
     if first_step:
         assert w.cow.shape[0] > 0
-    got, d = run_gpu(w, out_dt="f32", return_pools=True)
+    got, d = run_gpu(w, out_dt="f32", return_pools=True, flags=lib.PA_DECODE_SHARED_BLOCKS)
     assert_close(got, cfg_ref(4, first_step=first_step), "bf16", "f32", "cfg4")
     kp, vp, _, _ = _host_after_step(w)
     assert np.array_equal(d.k_cache.view(torch.int16).cpu().numpy().view(np.uint16), kp)
     assert np.array_equal(d.v_cache.view(torch.int16).cpu().numpy().view(np.uint16), vp)
+    # the shared-blocks flag is a cache hint only: same bits without it
+    assert np.array_equal(run_gpu(w, out_dt="f32"), got)
 
 
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
@@ -188,6 +191,17 @@ def test_small_parity(cdt, qdt, hq, hkv, D, B, variant, part):
     if qdt != "f32":
         got16 = run_gpu(w, out_dt=qdt, part=part, variant=variant)
         assert_close(got16, run_oracle(w), cdt, qdt, "16-bit output")
+
+
+@pytest.mark.parametrize("cdt,qdt,hq,hkv,variant", [("f16", "f16", 4, 4, 1), ("bf16", "bf16", 8, 2, 2),
+                                                    ("fp8", "bf16", 8, 2, 2), ("fp8", "f16", 4, 4, 1)])
+def test_shared_blocks_flag_is_only_a_cache_hint(cdt, qdt, hq, hkv, variant):
+    w = make_workload(list(SMALL_LENS), num_heads=hq, num_kv_heads=hkv, head_dim=128, dtype=cdt,
+                      q_dtype=qdt, seed=77)
+    a = run_gpu(w, out_dt="f32", part=256, variant=variant)
+    b = run_gpu(w, out_dt="f32", part=256, variant=variant, flags=lib.PA_DECODE_SHARED_BLOCKS)
+    assert np.array_equal(a, b)
+    assert_close(b, run_oracle(w), cdt, "f32", "shared-blocks flag")
 
 
 def test_mfma_rejects_more_than_16_heads_per_kv_head():
