@@ -170,7 +170,7 @@ def main():
     flags = lib.PA_DECODE_SHARED_BLOCKS if shared else 0
     reps = [upload(w) for _ in range(max(1, args.replicas))]
     out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(w.q_dtype), device="cuda")
-    ws = workspace_for(reps[0].q, reps[0].tables, w.block_size, args.partition)
+    ws = workspace_for(reps[0].q, reps[0].k_cache, reps[0].tables, w.block_size, args.partition)
 
     def step(i):
         d = reps[i % len(reps)]

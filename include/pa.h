@@ -128,11 +128,14 @@ int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_ca
                  int num_blocks, int max_tokens, pa_dtype cache_dtype, void* stream);
 
 /*
- * pa_decode_workspace_bytes -- bytes of workspace pa_decode needs for these sizes (0 when no
- * sequence can span more than one partition). partition_tokens as for pa_decode.
+ * pa_decode_workspace_bytes -- bytes of workspace pa_decode needs for these sizes. With an
+ * explicit partition_tokens this is exactly the fixed-partition need (0 when no sequence can span
+ * more than one partition); with partition_tokens = 0 it is an upper bound that covers whichever
+ * default plan pa_decode picks (fixed partitions, or the balanced split of the work over one
+ * resident grid, whose partial results take at most 2 * 2048 slots of Hq / Hkv heads).
  * Returns 0 as well for invalid sizes; pa_decode then reports the error.
  */
-size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int max_blocks_per_seq, int block_size, int partition_tokens);
 
 /*

@@ -34,6 +34,7 @@
 
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_sched.h"
 
 namespace pa {
 
@@ -91,22 +92,24 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 constexpr int kFp8BlocksPerIter = 2;
 constexpr int mfma_blocks_per_iter(int elem_bytes) { return elem_bytes == 2 ? 2 : kFp8BlocksPerIter; }
 
-// Bytes of dynamic LDS the kernel needs: the staged key tiles of one iteration per wave, reused
-// by the end-of-work-group merge.
+// Bytes of dynamic LDS: the staged key tiles of one iteration per wave (reused by the merge of
+// the four waves at the end of a segment) plus, for the balanced split, the batch's lengths and
+// block prefix sums.
 template <int CDT, int D>
-constexpr size_t mfma_lds_bytes(int G) {
+constexpr size_t mfma_lds_bytes(int G, int S, bool balanced) {
   const size_t stage =
       size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes;
   const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
-  return stage > merge ? stage : merge;
+  const size_t sched = balanced ? (2 * static_cast<size_t>(S) + 1) * sizeof(int) : 0;
+  return (stage > merge ? stage : merge) + sched;
 }
 
-// Launch bounds ask for 3 wave64s per SIMD (at most 168 VGPRs + AGPRs per lane): 2 leaves too
-// few tiles in flight per CU, 4 forces spills.
-// NT: non-temporal K/V loads (streaming; the default) or cached ones (blocks shared between
-// sequences of the batch).
+// One segment: blocks [b0, b1) of unit (sequence s, kv head g) -- all G query heads of the group.
+// The result is either the unit's final output (the segment covers all of it) or a partial result
+// in workspace slot `slot`. Every thread of the work-group calls it (it synchronises).
 template <int CDT, int QDT, int D, bool NT>
-__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, int s, int g, int L,
+                                             int b0, int b1, bool final_out, size_t slot) {
   constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int KK = D / 32;                 // score MFMAs per block
@@ -119,25 +122,10 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NBI = mfma_blocks_per_iter(EB);  // blocks per iteration (16 KB in flight)
   constexpr int kKeyAux = NT ? 2 : 0;        // cache policy of the key loads (2: non-temporal)
   constexpr bool kNtV = NT;
-  extern __shared__ float smem[];
-  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, n = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
-  const int nblk = (L + B - 1) / B;
-  const int b0 = p * a.part_blocks;
-  if (b0 >= nblk) {
-    if (p == 0)
-      for (int idx = tid; idx < G * D; idx += 256)
-        store_out(a.out, (static_cast<size_t>(s) * Hq + g * G) * D + idx, 0.0f, a.out_dtype);
-    return;
-  }
-  const int b1 = min(nblk, b0 + a.part_blocks);
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
 
   u32x4 qop[KK];
   if (n < G) {
@@ -170,6 +158,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), lsum = 0.0f;
+
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   // this wave's blocks are b0 + wave + 4*i, taken NBI per iteration; their table entries are
@@ -315,6 +304,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();  // every wave is done with its staged key tiles: the LDS is reused below
 
+
   // per-column sum over the four lane groups, then merge the four waves through LDS
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
@@ -345,33 +335,100 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
       num = __builtin_fmaf(e, sm_o[(w * G + nn) * D + d], num);
       den = __builtin_fmaf(e, sm_l[w * 16 + nn], den);
     }
-    const int h = g * G + nn;
     const float o = num / den;
-    if (nparts == 1) {
-      store_out(a.out, (static_cast<size_t>(s) * Hq + h) * D + d, o, a.out_dtype);
+    if (final_out) {
+      store_out(a.out, (static_cast<size_t>(s) * Hq + g * G + nn) * D + d, o, a.out_dtype);
     } else {
-      const size_t pi = (static_cast<size_t>(s) * Hq + h) * a.max_parts + p;
-      a.ws_o[pi * D + d] = o;
-      if (d == 0) a.ws_ml[pi] = make_float2(M, den);
+      a.ws_o[(slot * G + nn) * D + d] = o;
+      if (d == 0) a.ws_ml[slot * G + nn] = make_float2(M, den);
     }
   }
+  __syncthreads();  // the LDS is free for the next segment
+}
+
+// Fixed partitions: grid (kv head, sequence, partition); one segment per work-group.
+// Launch bounds ask for 3 wave64s per SIMD (at most 168 VGPRs + AGPRs per lane): 2 leaves too
+// few tiles in flight per CU, 4 forces spills.
+// NT: non-temporal K/V loads (streaming; the default) or cached ones (blocks shared between
+// sequences of the batch).
+template <int CDT, int QDT, int D, bool NT>
+__global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
+  const int Hq = a.num_heads, G = Hq / a.num_kv_heads;
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
+  const int nblk = (L + 15) / 16;
+  const int b0 = p * a.part_blocks;
+  if (b0 >= nblk) {
+    if (p == 0)
+      for (int idx = threadIdx.x; idx < G * D; idx += 256)
+        store_out(a.out, (static_cast<size_t>(s) * Hq + g * G) * D + idx, 0.0f, a.out_dtype);
+    return;
+  }
+  const int b1 = min(nblk, b0 + a.part_blocks);
+  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+  mfma_segment<CDT, QDT, D, NT>(a, smem, s, g, L, b0, b1, nparts == 1,
+                                (static_cast<size_t>(s) * a.num_kv_heads + g) * a.max_parts + p);
+}
+
+// Balanced split: work-group i of a.nw takes tiles [i*W/nw, (i+1)*W/nw) of the flattened
+// (sequence, kv head, block) list and walks them unit by unit.
+template <int CDT, int QDT, int D, bool NT>
+__global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  constexpr int B = 16;
+  constexpr int EB = Elem<CDT>::bytes;
+  const size_t stage = mfma_lds_bytes<CDT, D>(a.num_heads / a.num_kv_heads, 0, false);
+  int* lens_lds = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) + stage);
+  int* pref = lens_lds + a.num_seqs;
+  scan_batch(a, B, lens_lds, pref);
+  const long long hu = a.num_kv_heads;
+  const long long W = static_cast<long long>(pref[a.num_seqs]) * hu;
+  const int i = blockIdx.x;
+  if (i == 0)
+    for (int k = threadIdx.x; k <= a.num_seqs; k += blockDim.x) a.ws_pref[k] = pref[k];
+  const int nw = balanced_groups(W, a.nw);
+  if (i >= nw) return;
+  const long long lo = share_lo(W, nw, i), hi = share_lo(W, nw, i + 1);
+  long long t = lo;
+  while (t < hi) {
+    const int s = find_seq(pref, a.num_seqs, hu, t);
+    const int nb = pref[s + 1] - pref[s];
+    const long long rel = t - static_cast<long long>(pref[s]) * hu;
+    const int g = static_cast<int>(rel / nb);
+    const int j = static_cast<int>(rel - static_cast<long long>(g) * nb);
+    const long long uend = t - j + nb;
+    const long long seg_end = hi < uend ? hi : uend;
+    const bool whole = (j == 0) && (seg_end == uend);
+    mfma_segment<CDT, QDT, D, NT>(a, smem, s, g, lens_lds[s], j, j + static_cast<int>(seg_end - t),
+                                  whole, static_cast<size_t>(2 * i + (t == lo ? 0 : 1)));
+    t = seg_end;
+  }
+  (void)EB;
+}
+
+template <int CDT, int QDT, int D>
+static hipError_t launch_mfma_dn(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.num_heads / a.num_kv_heads;
+  const size_t shm = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.balanced != 0);
+  if (a.balanced) {
+    const dim3 grid(a.nw);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, false>), grid, dim3(256), shm, st, a);
+  } else {
+    const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, false>), grid, dim3(256), shm, st, a);
+  }
+  return hipGetLastError();
 }
 
 template <int CDT, int QDT>
 static hipError_t launch_mfma_d(const DecodeArgs& a, int D, hipStream_t st) {
-  const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-  const int G = a.num_heads / a.num_kv_heads;
-  if (D == 64) {
-    const size_t shm = mfma_lds_bytes<CDT, 64>(G);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 64, false>), grid, dim3(256), shm, st, a);
-  } else if (D == 128) {
-    const size_t shm = mfma_lds_bytes<CDT, 128>(G);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, 128, false>), grid, dim3(256), shm, st, a);
-  }
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (D == 64) return launch_mfma_dn<CDT, QDT, 64>(a, st);
+  if (D == 128) return launch_mfma_dn<CDT, QDT, 128>(a, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, hipStream_t st) {
@@ -380,6 +437,26 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, hipS
   if (cdt == DT_FP8 && qdt == DT_F16) return launch_mfma_d<DT_FP8, DT_F16>(a, D, st);
   if (cdt == DT_FP8 && qdt == DT_BF16) return launch_mfma_d<DT_FP8, DT_BF16>(a, D, st);
   return hipErrorInvalidValue;
+}
+
+// Work-groups per CU the balanced kernel keeps resident (from the occupancy calculator).
+int mfma_groups_per_cu(int cdt, int qdt, int D, int G, int S, bool stream_kv) {
+  int n = 0;
+  const void* k = nullptr;
+#define PA_PICK(C, Q, DD)                                                                        \
+  if (cdt == C && qdt == Q && D == DD)                                                           \
+    k = stream_kv ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, true>)  \
+                  : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, false>);
+  PA_PICK(DT_F16, DT_F16, 64) PA_PICK(DT_F16, DT_F16, 128) PA_PICK(DT_BF16, DT_BF16, 64)
+  PA_PICK(DT_BF16, DT_BF16, 128) PA_PICK(DT_FP8, DT_F16, 64) PA_PICK(DT_FP8, DT_F16, 128)
+  PA_PICK(DT_FP8, DT_BF16, 64) PA_PICK(DT_FP8, DT_BF16, 128)
+#undef PA_PICK
+  if (k == nullptr) return 0;
+  size_t shm = 0;
+  if (cdt == DT_FP8) shm = D == 64 ? mfma_lds_bytes<DT_FP8, 64>(G, S, true) : mfma_lds_bytes<DT_FP8, 128>(G, S, true);
+  else shm = D == 64 ? mfma_lds_bytes<DT_BF16, 64>(G, S, true) : mfma_lds_bytes<DT_BF16, 128>(G, S, true);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, shm) != hipSuccess) return 0;
+  return n;
 }
 
 }  // namespace pa

@@ -25,6 +25,7 @@
 
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_sched.h"
 
 namespace pa {
 
@@ -192,11 +193,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-// One work-group of D threads per (query head, sequence): combines the sequence's partitions.
-// With per-partition maxima m_k, sums l_k and normalised outputs o_k (log2 domain):
+// One work-group of D threads per (query head, sequence): combines the partial results of the
+// head's unit. With per-part maxima m_k, sums l_k and normalised outputs o_k (log2 domain):
 //   out = sum_k w_k o_k / sum_k w_k,   w_k = l_k * exp2(m_k - max_k m_k).
-// The weights are computed once per partition into LDS; every thread then sums over partitions
-// in the same order (deterministic), with the partial-output loads unrolled.
+// Fixed partitions: the parts are the unit's partitions in order. Balanced split: the parts are
+// the partial results of the work-groups whose shares cut the unit, in share order (a unit held
+// whole by one work-group was written by it directly; an empty sequence gets a zero output here).
+// The weights are computed once per part into LDS; every thread then sums over parts in the same
+// order (deterministic), with the partial-output loads unrolled.
 constexpr int kMergeChunk = 1024;
 
 template <int D>
@@ -204,14 +208,41 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
   __shared__ float sw[kMergeChunk];
   __shared__ float sred[D / 64];
   const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > a.max_blocks * block_size ? a.max_blocks * block_size : L);
-  const int nblk = (L + block_size - 1) / block_size;
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-  if (nparts <= 1) return;
-  const size_t row = (static_cast<size_t>(s) * a.num_heads + h) * a.max_parts;
+  const int gu = a.heads_per_unit, x = h / gu, hn = h - x * gu;
+  const long long hu = a.num_heads / gu;
+  const size_t orow = (static_cast<size_t>(s) * a.num_heads + h) * D;
+  int count;                 // parts to combine
+  size_t first_slot = 0;     // fixed partitions: slots first_slot + k
+  int i0 = 0;                // balanced split: work-groups i0 .. i0 + count - 1
+  bool i0_first = false;     // ... and whether the unit is work-group i0's first unit
+  if (a.balanced) {
+    const int p0 = a.ws_pref[s], nb = a.ws_pref[s + 1] - p0;
+    if (nb == 0) {
+      store_out(a.out, orow + d, 0.0f, a.out_dtype);
+      return;
+    }
+    const long long W = static_cast<long long>(a.ws_pref[a.num_seqs]) * hu;
+    const int nw = balanced_groups(W, a.nw);
+    const long long ustart = static_cast<long long>(p0) * hu + static_cast<long long>(x) * nb;
+    i0 = share_owner(W, nw, ustart);
+    const int i1 = share_owner(W, nw, ustart + nb - 1);
+    if (i0 == i1) return;  // one work-group took the whole unit and wrote its output
+    count = i1 - i0 + 1;   // every share is non-empty, so each of these holds a partial result
+    i0_first = share_lo(W, nw, i0) == ustart;
+  } else {
+    int L = a.lens[s];
+    L = L < 0 ? 0 : (L > a.max_blocks * block_size ? a.max_blocks * block_size : L);
+    const int nblk = (L + block_size - 1) / block_size;
+    count = (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (count <= 1) return;
+    first_slot = (static_cast<size_t>(s) * hu + x) * a.max_parts;
+  }
+  auto slot_of = [&](int k) -> size_t {
+    if (!a.balanced) return first_slot + k;
+    return k == 0 ? static_cast<size_t>(2 * i0 + (i0_first ? 0 : 1)) : static_cast<size_t>(2 * (i0 + k));
+  };
   float M = neg_inf();
-  for (int k = d; k < nparts; k += D) M = fmaxf(M, a.ws_ml[row + k].x);
+  for (int k = d; k < count; k += D) M = fmaxf(M, a.ws_ml[slot_of(k) * gu + hn].x);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if ((d & 63) == 0) sred[d >> 6] = M;
@@ -220,23 +251,22 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
 #pragma unroll
   for (int i = 1; i < D / 64; ++i) M = fmaxf(M, sred[i]);
   float num = 0.0f, den = 0.0f;
-  for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
-    const int n = min(kMergeChunk, nparts - c0);
+  for (int c0 = 0; c0 < count; c0 += kMergeChunk) {
+    const int n = min(kMergeChunk, count - c0);
     for (int k = d; k < n; k += D) {
-      const float2 ml = a.ws_ml[row + c0 + k];
+      const float2 ml = a.ws_ml[slot_of(c0 + k) * gu + hn];
       sw[k] = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
     }
     __syncthreads();
-    const float* po = a.ws_o + (row + c0) * D + d;
 #pragma unroll 8
     for (int k = 0; k < n; ++k) {
       const float wk = sw[k];
       den += wk;
-      num = __builtin_fmaf(wk, po[static_cast<size_t>(k) * D], num);
+      num = __builtin_fmaf(wk, a.ws_o[(slot_of(c0 + k) * gu + hn) * D + d], num);
     }
     __syncthreads();
   }
-  store_out(a.out, (static_cast<size_t>(s) * a.num_heads + h) * D + d, num / den, a.out_dtype);
+  store_out(a.out, orow + d, num / den, a.out_dtype);
 }
 
 // ---- launchers ----------------------------------------------------------------------------------

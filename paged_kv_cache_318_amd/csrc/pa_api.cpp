@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_launch.h"
+#include "pa_sched.h"
 
 namespace {
 
@@ -20,7 +21,13 @@ namespace {
 // group per work-group: fewer, heavier work-groups, each paying a few microseconds to fetch its
 // length, table entries and first tiles) is best at 1024 when there are many (sequence, kv head)
 // units to spread over the CUs, and at 2048 when there are few (long sequences, split more).
-// Workspaces are sized for the shortest default, so they fit every choice.
+// With few units the MFMA kernel instead takes the balanced split (every work-group of one
+// resident grid reads the same number of tiles): on 16 sequences of 16K..32K tokens it cut the
+// kernel from 157 to 147 us, while on 128 sequences of 64..8192 tokens (1024 units) fixed 1024-
+// token partitions stay faster (151 us against 155..165 us for grids of 1x..4x the resident
+// work-groups), since there a work-group walks several short units, each starting with a latency
+// bubble the hardware's own dispatch of many small work-groups hides better.
+// Workspaces are sized for the largest of these plans, so they fit every choice.
 constexpr int kDefaultPartitionValu = 512;
 constexpr int kDefaultPartitionMfma = 1024;
 constexpr int kDefaultPartitionMfmaFewUnits = 2048;
@@ -67,8 +74,6 @@ void end_event(bool active, hipStream_t st, const EventPair& ev, int kind) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-int elem_bytes(int dt) { return dt == PA_F32 ? 4 : (dt == PA_FP8_E4M3 ? 1 : 2); }
-
 // Partition plan shared by workspace sizing and the launch.
 struct Plan {
   int part_blocks;
@@ -86,10 +91,36 @@ Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_token
   return Plan{pb, (max_blocks_per_seq + pb - 1) / pb};
 }
 
-size_t workspace_for(int num_seqs, int num_heads, int head_dim, const Plan& pl) {
+// Workspace of `slots` partial-result slots of `gu` heads each: normalised outputs [slots][gu][D]
+// (fp32) followed by (max, sum) pairs [slots][gu].
+size_t slot_bytes(size_t slots, int gu, int head_dim) {
+  return slots * gu * (static_cast<size_t>(head_dim) * sizeof(float) + 2 * sizeof(float));
+}
+
+// Fixed partitions: one slot per (unit, partition), S * Hq * max_parts heads in all.
+size_t fixed_workspace(int num_seqs, int num_heads, int head_dim, const Plan& pl) {
   if (pl.max_parts <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_heads * pl.max_parts *
-         (static_cast<size_t>(head_dim) * sizeof(float) + 2 * sizeof(float));
+  return slot_bytes(static_cast<size_t>(num_seqs) * num_heads * pl.max_parts, 1, head_dim);
+}
+
+// The balanced split: for batches of few (sequence, kv head) units (the partition defaults above
+// say why); it also needs the batch's lengths and block prefix sums in LDS and 32-bit block totals.
+bool balanced_eligible(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
+  return static_cast<long long>(num_seqs) * num_kv_heads < kFewUnits &&
+         num_seqs <= pa::kMaxBalancedSeqs &&
+         static_cast<int64_t>(num_seqs) * max_blocks_per_seq < (int64_t{1} << 31);
+}
+
+// CUs of the current device (cached per device; 0 if the runtime cannot tell).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -180,13 +211,24 @@ int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_ca
   return hip_status(e);
 }
 
-size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
-                                 int block_size, int partition_tokens) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0 || partition_tokens < 0)
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int max_blocks_per_seq, int block_size, int partition_tokens) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 || partition_tokens < 0)
     return 0;
-  return workspace_for(num_seqs, num_heads, head_dim,
-                       plan_partitions(max_blocks_per_seq, block_size, partition_tokens));
+  if (partition_tokens > 0)
+    return fixed_workspace(num_seqs, num_heads, head_dim,
+                           plan_partitions(max_blocks_per_seq, block_size, partition_tokens));
+  // default plan: fixed partitions of the shortest default length, or the balanced split
+  size_t need = fixed_workspace(num_seqs, num_heads, head_dim,
+                                plan_partitions(max_blocks_per_seq, block_size, 0));
+  if (balanced_eligible(num_seqs, num_kv_heads, max_blocks_per_seq)) {
+    const int G = num_heads / num_kv_heads;
+    const size_t bal = slot_bytes(2 * static_cast<size_t>(pa::kMaxBalancedGroups), G <= 16 ? G : 1, head_dim) +
+                       (pa::kMaxBalancedSeqs + 1) * sizeof(int);
+    need = need > bal ? need : bal;
+  }
+  return need;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -229,7 +271,22 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma,
                                   static_cast<long long>(num_seqs) * num_kv_heads);
   if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
-  const size_t need = workspace_for(num_seqs, num_heads, head_dim, pl);
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  // Default plan for the MFMA kernel on few units: the balanced split over one resident grid.
+  const bool balanced =
+      partition_tokens == 0 && use_mfma && balanced_eligible(num_seqs, num_kv_heads, max_blocks_per_seq);
+  int nw = 0;
+  if (balanced) {
+    const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, G, num_seqs, stream_kv);
+    const int cus = cu_count();
+    nw = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    nw = nw > pa::kMaxBalancedGroups ? pa::kMaxBalancedGroups : nw;
+  }
+  const int gu = use_mfma ? G : 1;
+  const size_t slots = balanced ? 2 * static_cast<size_t>(nw)
+                                : static_cast<size_t>(num_seqs) * (num_heads / gu) * pl.max_parts;
+  const size_t need = balanced ? slot_bytes(slots, gu, head_dim) + (num_seqs + 1) * sizeof(int)
+                               : fixed_workspace(num_seqs, num_heads, head_dim, pl);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a;
@@ -241,11 +298,13 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.lens = context_lens;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  const size_t o_bytes = need > 0 ? static_cast<size_t>(num_seqs) * num_heads * pl.max_parts *
-                                        head_dim * sizeof(float)
-                                  : 0;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = need > 0 ? reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + o_bytes) : nullptr;
+  a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need > 0 ? reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) +
+                                                 slots * gu * head_dim * sizeof(float))
+                     : nullptr;
+  a.ws_pref = balanced ? reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) +
+                                                slot_bytes(slots, gu, head_dim))
+                       : nullptr;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -255,7 +314,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.max_parts = pl.max_parts;
   a.out_dtype = out_dtype;
   a.zscale = scale * pa::kLog2e;
-  a.stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) ? 0 : 1;
+  a.stream_kv = stream_kv ? 1 : 0;
+  a.heads_per_unit = gu;
+  a.balanced = balanced ? 1 : 0;
+  a.nw = nw;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;
@@ -264,7 +326,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                           : pa::launch_decode_valu(a, cache_dtype, q_dtype, head_dim, block_size, st);
   end_event(timed, st, ev, PA_KERNEL_DECODE_PARTITION);
   if (e != hipSuccess) return PA_ERR_HIP;
-  if (pl.max_parts > 1) {
+  if (balanced || pl.max_parts > 1) {
     timed = begin_event(st, &ev);
     e = pa::launch_decode_merge(a, head_dim, block_size, st);
     end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);

@@ -148,11 +148,19 @@ struct DecodeArgs {
   const int32_t* lens;
   const float* k_scale;
   const float* v_scale;
-  float* ws_o;     // [S][Hq][max_parts][D]
-  float2* ws_ml;   // [S][Hq][max_parts] = (max of log2-scaled scores, sum of exp2)
+  // Partial results, one slot per (unit, partition) -- fixed partitions: slot
+  // (s * units + x) * max_parts + p; balanced split: slot 2 * work-group + {0: its first unit,
+  // 1: its last}. A slot holds the unit's heads_per_unit heads: ws_o[slot][head][D] normalised
+  // outputs and ws_ml[slot][head] = (max of log2-scaled scores, sum of exp2).
+  float* ws_o;
+  float2* ws_ml;
+  int* ws_pref;    // balanced split: block prefix sums [S + 1] (written by work-group 0)
   int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks;
   int part_blocks, max_parts, out_dtype;
   int stream_kv;   // 1: K/V read non-temporally; 0: through the caches (shared blocks)
+  int heads_per_unit;  // query heads one work-group accumulates: 1 (VALU) or Hq / Hkv (MFMA)
+  int balanced;    // 1: balanced split over nw work-groups; 0: fixed partitions
+  int nw;
   float zscale;    // softmax scale * log2(e)
 };
 

@@ -34,7 +34,7 @@ _SIGS = {
     "pa_copy_blocks": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "pa_gather_kv": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                       _vp], _i32),
-    "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                    _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_diag_read_bandwidth": ([_vp, _sz, _vp, _i32, _i32, _vp, _vp], _i32),
@@ -148,11 +148,11 @@ def pa_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens, str
         _ptr(context_lens), S, Hkv, D, B, MB, NB, max_tokens, dtype_code(k_cache), _stream(stream)))
 
 
-def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                               max_blocks_per_seq: int, block_size: int,
                               partition_tokens: int = 0) -> int:
-    return int(load().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq,
-                                                block_size, partition_tokens))
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                max_blocks_per_seq, block_size, partition_tokens))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, k_scale=None,

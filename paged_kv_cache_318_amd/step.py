@@ -27,9 +27,11 @@ def decode_step(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_n
                   stream=stream, flags=flags)
 
 
-def workspace_for(q, block_tables, block_size: int, partition_tokens: int = 0):
-    """A uint8 GPU tensor sized for pa_decode (None when no workspace is needed)."""
+def workspace_for(q, k_cache, block_tables, block_size: int, partition_tokens: int = 0):
+    """A uint8 GPU tensor sized for pa_decode (None when no workspace is needed); ``k_cache`` is the
+    key pool [num_blocks][num_kv_heads][block_size][head_dim]."""
     import torch
     S, Hq, D = q.shape
-    n = lib.pa_decode_workspace_bytes(S, Hq, D, block_tables.shape[1], block_size, partition_tokens)
+    n = lib.pa_decode_workspace_bytes(S, Hq, k_cache.shape[1], D, block_tables.shape[1], block_size,
+                                      partition_tokens)
     return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=q.device)

@@ -64,11 +64,19 @@ def test_status_strings_and_version(L):
 
 def test_workspace_bytes(L):
     # one partition per sequence -> no workspace
-    assert L.pa_decode_workspace_bytes(64, 40, 128, 8, 16, 512) == 0
+    assert L.pa_decode_workspace_bytes(64, 40, 40, 128, 8, 16, 512) == 0
     # 2048 tokens in 512-token partitions -> 4 partials of (D + 2) floats per (seq, head)
-    assert L.pa_decode_workspace_bytes(64, 40, 128, 128, 16, 512) == 64 * 40 * 4 * (128 + 2) * 4
-    assert L.pa_decode_workspace_bytes(16, 32, 128, 2048, 16, 0) == 16 * 32 * 64 * 130 * 4
-    assert L.pa_decode_workspace_bytes(0, 40, 128, 8, 16, 0) == 0
+    assert L.pa_decode_workspace_bytes(64, 40, 40, 128, 128, 16, 512) == 64 * 40 * 4 * (128 + 2) * 4
+    # default plan: the larger of the 512-token fixed plan and the balanced split's 2 * 2048
+    # slots of Hq / Hkv heads (plus the block prefix sums of up to 1024 sequences)
+    assert L.pa_decode_workspace_bytes(16, 32, 32, 128, 2048, 16, 0) == 16 * 32 * 64 * 130 * 4
+    assert L.pa_decode_workspace_bytes(4, 32, 4, 128, 64, 16, 0) == 2 * 2048 * 8 * 130 * 4 + 1025 * 4
+    # batches of 256 or more (sequence, kv head) units get the fixed plans only
+    assert L.pa_decode_workspace_bytes(2048, 8, 1, 128, 8, 16, 0) == 0
+    assert L.pa_decode_workspace_bytes(128, 32, 8, 128, 512, 16, 0) == 128 * 32 * 16 * 130 * 4
+    for bad in [(0, 40, 40, 128, 8, 16, 0), (4, 40, 0, 128, 8, 16, 0), (4, 40, 3, 128, 8, 16, 0),
+                (4, 40, 40, 128, 8, 16, -1)]:
+        assert L.pa_decode_workspace_bytes(*bad) == 0
 
 
 def _decode(L, **kw):

@@ -82,7 +82,7 @@ def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False, flags=0):
     d = upload(w)
     out_dt = out_dt or w.q_dtype
     out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(out_dt), device="cuda")
-    ws = workspace_for(d.q, d.tables, w.block_size, part)
+    ws = workspace_for(d.q, d.k_cache, d.tables, w.block_size, part)
     decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
                 w.scale, d.k_scale, d.v_scale, partition_tokens=part, variant=variant, workspace=ws,
                 flags=flags)
@@ -191,6 +191,24 @@ def test_small_parity(cdt, qdt, hq, hkv, D, B, variant, part):
     if qdt != "f32":
         got16 = run_gpu(w, out_dt=qdt, part=part, variant=variant)
         assert_close(got16, run_oracle(w), cdt, qdt, "16-bit output")
+
+
+@pytest.mark.parametrize("lens", [[8192 + 5], [1, 0, 5000, 17, 3000, 16, 0, 2049], [40] * 1100],
+                         ids=["one-long", "mixed-with-empty", "many-units"])
+@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
+def test_balanced_split_cuts_units(lens, cdt):
+    """On batches of few (sequence, kv head) units the MFMA kernel's default plan spreads the K/V
+    evenly over one resident grid: a lone long unit is cut across many work-groups, and empty
+    sequences sit between cut units; a batch of many units takes fixed partitions instead.
+    Explicit partitions give the same result within tolerance."""
+    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype="bf16",
+                      seed=len(lens) + 7)
+    ref = run_oracle(w)
+    got = run_gpu(w, out_dt="f32", variant=2)
+    assert_close(got, ref, cdt, "f32", f"balanced {cdt} S={len(lens)}")
+    fixed = run_gpu(w, out_dt="f32", part=512, variant=2)
+    assert np.max(np.abs(got - fixed)) <= TOL[cdt]
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", variant=2))
 
 
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,variant", [("f16", "f16", 4, 4, 1), ("bf16", "bf16", 8, 2, 2),
