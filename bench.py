@@ -47,7 +47,155 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--measure", default="step", choices=("step", "swap", "paging"),
+                   help="step: the decode-step line (default); swap: block swap to and from pinned "
+                        "host memory; paging: paged vs contiguous placement and block sizes")
     return p.parse_args()
+
+
+def timing_batch(lens, num_heads, num_kv_heads, head_dim, block_size, dtype, placement, seed,
+                 free_fraction=0.2):
+    """Device inputs for timing only (no oracle check): tables from the block manager -- blocks
+    handed out in a seeded random order, or in address order for ``placement="contiguous"`` --
+    and K/V/q drawn on the GPU (seeded N(0,1)), which takes milliseconds instead of the host
+    generator's seconds."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_318_amd.blocks import BlockPool
+
+    B = block_size
+    used = sum(-(-int(L) // B) for L in lens)
+    NB = max(1, int(np.ceil((1.0 + free_fraction) * used)))
+    rng = np.random.default_rng(seed)
+    order = np.arange(NB) if placement == "contiguous" else rng.permutation(NB)
+    pool = BlockPool(NB, B, free_order=order.tolist())
+    for s, L in enumerate(lens):
+        pool.add_sequence(s, int(L))
+    tables = pool.block_table(list(range(len(lens))))
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    dev = "cuda"
+    return {
+        "q": torch.randn(len(lens), num_heads, head_dim, generator=g, device=dev).to(tdt),
+        "k": torch.randn(NB, num_kv_heads, B, head_dim, generator=g, device=dev).to(tdt),
+        "v": torch.randn(NB, num_kv_heads, head_dim, B, generator=g, device=dev).to(tdt),
+        "tables": torch.from_numpy(tables).to(dev),
+        "lens": torch.tensor(np.asarray(lens, dtype=np.int32), device=dev),
+        "num_blocks": NB, "used_blocks": used, "table_np": tables,
+    }
+
+
+def measure_swap(args, lib, torch):
+    """Preemption by swapping: the blocks of the first half of the batch go out to a pinned host
+    pool and come back (PA_SWAP_OUT, then PA_SWAP_IN), against the runtime's own copies of the
+    same number of contiguous bytes in each direction (the host link's ceiling)."""
+    import numpy as np
+
+    from workloads.synth import config_lens
+    spec = config_lens(args.config if args.config in (2, 3) else 2)
+    b = timing_batch(spec["lens"], spec["num_heads"], spec["num_kv_heads"], spec["head_dim"], 16,
+                     spec["dtype"], "scattered", seed=args.config)
+    half = len(spec["lens"]) // 2
+    blocks = np.concatenate([b["table_np"][s, : -(-int(L) // 16)]
+                             for s, L in enumerate(spec["lens"][:half])]).astype(np.int32)
+    n = blocks.size
+    hk = torch.empty((n,) + tuple(b["k"].shape[1:]), dtype=b["k"].dtype, pin_memory=True)
+    hv = torch.empty((n,) + tuple(b["v"].shape[1:]), dtype=b["v"].dtype, pin_memory=True)
+    idx = np.arange(n, dtype=np.int32)
+    out_pairs = torch.from_numpy(np.stack([blocks, idx], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([idx, blocks], 1)).cuda()
+    nbytes = 2 * n * b["k"][0].numel() * b["k"].element_size()
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    t_out = timed(lambda: lib.pa_swap_blocks(b["k"], b["v"], hk, hv, out_pairs, lib.PA_SWAP_OUT))
+    t_in = timed(lambda: lib.pa_swap_blocks(b["k"], b["v"], hk, hv, in_pairs, lib.PA_SWAP_IN))
+    dev_buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    host_buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    t_d2h = timed(lambda: host_buf.copy_(dev_buf, non_blocking=True))
+    t_h2d = timed(lambda: dev_buf.copy_(host_buf, non_blocking=True))
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    line = {
+        "metric": "block swap between HBM and pinned host memory: GB/s per direction",
+        "value": gbs(max(t_out, t_in)), "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": spec["dtype"], "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": f"swap-{spec['name']}", "blocks": int(n), "bytes_per_direction": nbytes,
+                   "block_bytes_kv": 2 * b["k"][0].numel() * b["k"].element_size()},
+        "swap_out_gbs": gbs(t_out), "swap_in_gbs": gbs(t_in),
+        "runtime_copy_d2h_gbs": gbs(t_d2h), "runtime_copy_h2d_gbs": gbs(t_h2d),
+        "ms": {"swap_out": round(t_out, 3), "swap_in": round(t_in, 3), "copy_d2h": round(t_d2h, 3),
+               "copy_h2d": round(t_h2d, 3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def measure_paging(args, lib, torch):
+    """The pages say the paged kernel pays for its indirection and that the block size trades
+    table overhead against the unused tail. Same kernel, same lengths: blocks scattered through the
+    pool vs handed out in address order (every sequence contiguous), for block sizes 8, 16 and 32,
+    on the MHA batch (VALU kernel) and the GQA batch (MFMA kernel at 16, VALU otherwise)."""
+    from paged_kv_cache_318_amd.step import workspace_for
+    from workloads.synth import config_lens
+    rows = []
+    for cfg in (2, 3):
+        spec = config_lens(cfg)
+        for B in (8, 16, 32):
+            for placement in ("scattered", "contiguous"):
+                b = timing_batch(spec["lens"], spec["num_heads"], spec["num_kv_heads"],
+                                 spec["head_dim"], B, spec["dtype"], placement, seed=cfg)
+                out = torch.empty_like(b["q"])
+                ws = workspace_for(b["q"], b["k"], b["tables"], B)
+                scale = spec["head_dim"] ** -0.5
+
+                def call():
+                    lib.pa_decode(out, b["q"], b["k"], b["v"], b["tables"], b["lens"], scale,
+                                  workspace=ws)
+
+                for _ in range(5):
+                    call()
+                torch.cuda.synchronize()
+                lib.pa_profile_enable(True)
+                for _ in range(args.steps):
+                    call()
+                torch.cuda.synchronize()
+                k_ms, k_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
+                m_ms, m_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
+                lib.pa_profile_enable(False)
+                tokens = int(sum(spec["lens"]))
+                kv = tokens * 2 * spec["num_kv_heads"] * spec["head_dim"] * b["k"].element_size()
+                us = 1e3 * k_ms / max(k_n, 1)
+                G = spec["num_heads"] // spec["num_kv_heads"]
+                rows.append({
+                    "workload": spec["name"], "block_size": B, "placement": placement,
+                    "kernel": "decode_mfma" if (B == 16 and G >= 2) else "decode_valu",
+                    "attention_us": round(us, 2),
+                    "merge_us": round(1e3 * m_ms / m_n, 2) if m_n else None,
+                    "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
+                    "table_entries": int(sum(-(-int(L) // B) for L in spec["lens"])),
+                    "unused_tail_slots": int(sum(-(-int(L) // B) * B - int(L) for L in spec["lens"])),
+                })
+                print(f"[bench] paging {rows[-1]}", file=sys.stderr, flush=True)
+                del b, out, ws
+    for r in rows:
+        twin = [x for x in rows if x["workload"] == r["workload"] and x["block_size"] == r["block_size"]
+                and x["placement"] == "contiguous"][0]
+        r["vs_contiguous"] = round(r["attention_us"] / twin["attention_us"], 4)
+    line = {"metric": "paged vs contiguous placement and block size: attention kernel time",
+            "unit": "us", "n_gpus": 1, "higher_is_better": False, "steps": args.steps,
+            "data": "synthetic (seeded, generated on the GPU)", "rows": rows}
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -150,6 +298,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     lib.load()
+    if args.measure == "swap":
+        return measure_swap(args, lib, torch)
+    if args.measure == "paging":
+        return measure_paging(args, lib, torch)
     over = {}
     if args.dtype:
         over["dtype"] = args.dtype

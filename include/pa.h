@@ -174,6 +174,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_swap_blocks -- move whole blocks between the device pool and a host pool in pinned memory,
+ * to preempt a group of sequences and resume it later ("vLLM и PagedAttention" (podcast
+ * transcript), paragraph on preemption: a group's KV data can be moved to CPU memory and brought
+ * back, at the speed of the host link).
+ *
+ *   k_cache, v_cache (+ k_scale, v_scale): the device pool, num_blocks blocks, layout above.
+ *   host_k, host_v (+ host_k_scale, host_v_scale): a host pool of num_host_blocks blocks in the
+ *     same layout, in pinned host memory (hipHostMalloc, or a pinned torch tensor).
+ *   block_pairs: int32 [num_pairs][2] = (src, dst), in device memory or pinned host memory.
+ *     PA_SWAP_OUT: device block src -> host block dst. PA_SWAP_IN: host block src -> device
+ *     block dst. Both caches, every kv head, and for fp8 caches both scales. The dsts must be
+ *     distinct; a pair naming a block outside its pool is skipped.
+ *   Scales: required on both sides for PA_FP8_E4M3 caches, ignored otherwise.
+ * Every pointer's kind is checked with hipPointerGetAttributes before the launch: a device
+ * pointer that is not device memory, or a host pointer that is not pinned, returns
+ * PA_ERR_INVALID_ARG (pageable host memory cannot be read by the kernel). The kernel accesses the
+ * host pool directly over the host link; the host pool must stay allocated until the stream has
+ * passed the call. num_pairs == 0 is a no-op.
+ */
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
+
+int pa_swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int num_blocks,
+                   void* host_k, void* host_v, float* host_k_scale, float* host_v_scale,
+                   int num_host_blocks, const int32_t* block_pairs, int num_pairs, int direction,
+                   int num_kv_heads, int head_dim, int block_size, pa_dtype cache_dtype,
+                   void* stream);
+
+/*
  * Profiling: when enabled, every pa_* launch is bracketed by HIP events on its stream.
  * pa_profile_read synchronises on those events and returns, for one kernel kind, the summed
  * device time in milliseconds and the number of launches since the last reset.
@@ -183,7 +211,8 @@ typedef enum {
   PA_KERNEL_DECODE_MERGE = 1,     /* the log-sum-exp merge of partitions              */
   PA_KERNEL_WRITE_KV = 2,
   PA_KERNEL_COPY_BLOCKS = 3,
-  PA_KERNEL_GATHER_KV = 4
+  PA_KERNEL_GATHER_KV = 4,
+  PA_KERNEL_SWAP_BLOCKS = 5
 } pa_kernel_kind;
 
 int pa_profile_enable(int on);  /* also resets the counters */

@@ -49,7 +49,7 @@ import numpy as np
 
 __all__ = [
     "E4M3_VALUES", "e4m3_decode", "e4m3_encode", "fp8_quantize",
-    "to_f64", "write_kv", "copy_blocks", "gather_sequence", "sequence_kv",
+    "to_f64", "write_kv", "copy_blocks", "swap_blocks", "gather_sequence", "sequence_kv",
     "attention_contiguous", "attention_blockwise", "attention_split",
     "decode", "decode_blockwise", "decode_split",
     "kv_bytes_per_token", "unused_slots",
@@ -171,6 +171,23 @@ def copy_blocks(k_pool, v_pool, pairs, k_scale=None, v_scale=None):
         if k_scale is not None:
             k_scale[dst] = k_scale[src].copy()
             v_scale[dst] = v_scale[src].copy()
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, src_ks=None, src_vs=None, dst_ks=None,
+                dst_vs=None):
+    """Preemption by swapping ([Transcript], the paragraph on preemption: a group's KV data moves
+    to CPU memory and later comes back): for each (src, dst) pair, block ``dst`` of the destination
+    pool becomes a copy of block ``src`` of the source pool -- every head's keys and values, and
+    the fp8 scales when given. A pair naming a block outside its pool is skipped (the library's
+    contract for unvalidated device contents)."""
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        if not (0 <= src < src_k.shape[0] and 0 <= dst < dst_k.shape[0]):
+            continue
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+        if src_ks is not None:
+            dst_ks[dst] = src_ks[src]
+            dst_vs[dst] = src_vs[src]
 
 
 # --------------------------------------------------------------------------------------------

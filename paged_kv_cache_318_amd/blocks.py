@@ -20,10 +20,17 @@ Rules, by page title and section:
 * "Paged Attention" study notes, section "块分配策略" (block allocation): allocation fails with
   an out-of-memory error when the free list is too short. Unlike those notes, ``free`` here
   honours reference counts, and allocation never needs contiguous blocks.
+* "vLLM и PagedAttention" (podcast transcript), paragraph on preemption: when running sequences
+  need blocks and none are free, a whole group is suspended -- the next attention step needs every
+  block of a sequence, so eviction is all-or-nothing per group -- and its KV data either moves to
+  CPU memory and comes back later, or is dropped and recomputed. ``swap_out`` / ``swap_in`` keep
+  the host side of the first option: a second pool of host blocks with its own free list.
 
 Readings where the pages are open: the sequence that triggers a copy gets the copy and the source
 block's count drops by one; the last remaining holder (count 1) writes in place; within one decode
-step sequences append in the order they are given.
+step sequences append in the order they are given. A swapped group must own its blocks outright
+(no block shared with a sequence outside the group); blocks shared inside the group stay shared
+on the host and after the swap back (one host block per distinct device block, and back).
 """
 
 from __future__ import annotations
@@ -48,9 +55,10 @@ class BlockPool:
     ``0 .. num_blocks-1``.
     """
 
-    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Iterable[int]] = None):
-        if num_blocks <= 0 or block_size <= 0:
-            raise ValueError("num_blocks and block_size must be positive")
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Iterable[int]] = None,
+                 num_host_blocks: int = 0):
+        if num_blocks <= 0 or block_size <= 0 or num_host_blocks < 0:
+            raise ValueError("num_blocks and block_size must be positive, num_host_blocks >= 0")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
@@ -60,6 +68,12 @@ class BlockPool:
         self.ref: List[int] = [0] * self.num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lengths: Dict[int, int] = {}
+        # host pool for swapped-out groups: free list, refcounts, and the swapped sequences'
+        # tables of host block ids
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_free: deque = deque(range(self.num_host_blocks))
+        self.host_ref: List[int] = [0] * self.num_host_blocks
+        self.swapped: Dict[int, List[int]] = {}
 
     # -- allocation ---------------------------------------------------------------------------
     def _take(self, n: int) -> List[int]:
@@ -116,12 +130,81 @@ class BlockPool:
         return table[j] * self.block_size + off, cow
 
     def free_sequence(self, seq_id: int) -> None:
-        """Drop a finished sequence; blocks whose count reaches zero return to the free pool."""
-        for b in self.tables.pop(seq_id):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+        """Drop a finished (or swapped-out) sequence; blocks whose count reaches zero return to
+        their pool's free list."""
+        if seq_id in self.swapped:
+            for h in self.swapped.pop(seq_id):
+                self.host_ref[h] -= 1
+                if self.host_ref[h] == 0:
+                    self.host_free.append(h)
+        else:
+            for b in self.tables.pop(seq_id):
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self.free.append(b)
         del self.lengths[seq_id]
+
+    # -- preemption by swapping --------------------------------------------------------------------
+    @staticmethod
+    def _distinct(tables: Iterable[List[int]]) -> List[int]:
+        seen: Dict[int, None] = {}
+        for t in tables:
+            for b in t:
+                seen.setdefault(b, None)
+        return list(seen)
+
+    def swap_out(self, seq_ids: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move a group's blocks to the host pool. Returns the ``(device block, host block)`` pairs
+        to copy (``pa_swap_blocks`` with PA_SWAP_OUT) before the freed device blocks are reused.
+        Raises ``ValueError`` if a block is also used outside the group, ``OutOfBlocks`` if the
+        host pool is short; the state is then unchanged."""
+        group = list(dict.fromkeys(seq_ids))
+        for s in group:
+            if s not in self.tables:
+                raise ValueError(f"sequence {s} is not resident")
+        dev = self._distinct(self.tables[s] for s in group)
+        inside: Dict[int, int] = {}
+        for s in group:
+            for b in self.tables[s]:
+                inside[b] = inside.get(b, 0) + 1
+        if any(self.ref[b] != inside[b] for b in dev):
+            raise ValueError("a block of the group is shared with a sequence outside it")
+        if len(dev) > len(self.host_free):
+            raise OutOfBlocks(f"need {len(dev)} free host blocks, have {len(self.host_free)}")
+        to_host = {b: self.host_free.popleft() for b in dev}
+        for b in dev:
+            self.host_ref[to_host[b]] = self.ref[b]
+            self.ref[b] = 0
+            self.free.append(b)
+        for s in group:
+            self.swapped[s] = [to_host[b] for b in self.tables.pop(s)]
+        return [(b, to_host[b]) for b in dev]
+
+    def swap_in(self, seq_ids: Sequence[int]) -> List[Tuple[int, int]]:
+        """Bring a swapped-out group back into device blocks (taken from the front of the free
+        list). Returns the ``(host block, device block)`` pairs to copy (PA_SWAP_IN) before the
+        group runs again. The group must hold every reference to its host blocks; raises
+        ``OutOfBlocks`` if the device pool is short, leaving the state unchanged."""
+        group = list(dict.fromkeys(seq_ids))
+        for s in group:
+            if s not in self.swapped:
+                raise ValueError(f"sequence {s} is not swapped out")
+        host = self._distinct(self.swapped[s] for s in group)
+        inside: Dict[int, int] = {}
+        for s in group:
+            for h in self.swapped[s]:
+                inside[h] = inside.get(h, 0) + 1
+        if any(self.host_ref[h] != inside[h] for h in host):
+            raise ValueError("a host block of the group is shared with a sequence outside it")
+        dev = self._take(len(host))
+        to_dev = dict(zip(host, dev))
+        for h in host:
+            self.ref[to_dev[h]] = self.host_ref[h]
+            self.host_ref[h] = 0
+            self.host_free.append(h)
+        for s in group:
+            self.tables[s] = [to_dev[h] for h in self.swapped.pop(s)]
+        return [(h, to_dev[h]) for h in host]
 
     # -- views ----------------------------------------------------------------------------------
     def block_table(self, seq_ids: Sequence[int], width: Optional[int] = None) -> np.ndarray:
@@ -155,3 +238,15 @@ class BlockPool:
         used = {b for b in range(self.num_blocks) if self.ref[b] > 0}
         assert not (free & used), "a referenced block is on the free list"
         assert free | used == set(range(self.num_blocks)), "a block is neither free nor referenced"
+        href = [0] * self.num_host_blocks
+        for s, t in self.swapped.items():
+            assert s not in self.tables, f"seq {s} is both resident and swapped out"
+            assert len(t) == self.blocks_needed(self.lengths[s]), f"seq {s}: host table/length mismatch"
+            for h in t:
+                href[h] += 1
+        assert href == self.host_ref, "host reference counts differ from the swapped tables"
+        hfree = set(self.host_free)
+        assert len(hfree) == len(self.host_free), "a host block appears twice in the free list"
+        hused = {h for h in range(self.num_host_blocks) if self.host_ref[h] > 0}
+        assert not (hfree & hused) and hfree | hused == set(range(self.num_host_blocks)), \
+            "host pool: a block is both free and used, or neither"

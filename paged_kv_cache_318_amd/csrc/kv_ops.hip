@@ -106,18 +106,23 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ 
   }
 }
 
-// grid.x = pair, grid.y = chunk of the block; 16-byte copies of both caches.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* k_cache, uint8_t* v_cache,
-                                                          float* k_scale, float* v_scale,
-                                                          const int32_t* pairs, int NB,
-                                                          int Hkv, size_t block_bytes) {
+// grid.x = pair, grid.y = chunk of the block; 16-byte copies of both caches from block src of
+// the source pool to block dst of the destination pool (one pool for copy-on-write, so the two may
+// alias; the device pool and a pinned host pool for swaps). Pairs naming a block outside either
+// pool are skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const uint8_t* src_k, const uint8_t* src_v,
+                                                          uint8_t* dst_k, uint8_t* dst_v,
+                                                          const float* src_ks, const float* src_vs,
+                                                          float* dst_ks, float* dst_vs,
+                                                          const int32_t* pairs, int src_nb,
+                                                          int dst_nb, int Hkv, size_t block_bytes) {
   const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
-  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  if (src < 0 || src >= src_nb || dst < 0 || dst >= dst_nb) return;
   const size_t n16 = block_bytes / 16;
-  const u32x4* ks = reinterpret_cast<const u32x4*>(k_cache + static_cast<size_t>(src) * block_bytes);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(v_cache + static_cast<size_t>(src) * block_bytes);
-  u32x4* kd = reinterpret_cast<u32x4*>(k_cache + static_cast<size_t>(dst) * block_bytes);
-  u32x4* vd = reinterpret_cast<u32x4*>(v_cache + static_cast<size_t>(dst) * block_bytes);
+  const u32x4* ks = reinterpret_cast<const u32x4*>(src_k + static_cast<size_t>(src) * block_bytes);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(src_v + static_cast<size_t>(src) * block_bytes);
+  u32x4* kd = reinterpret_cast<u32x4*>(dst_k + static_cast<size_t>(dst) * block_bytes);
+  u32x4* vd = reinterpret_cast<u32x4*>(dst_v + static_cast<size_t>(dst) * block_bytes);
   for (size_t i = static_cast<size_t>(blockIdx.y) * blockDim.x + threadIdx.x; i < n16;
        i += static_cast<size_t>(gridDim.y) * blockDim.x) {
     const u32x4 a = ks[i];
@@ -125,10 +130,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* k_cache, uint
     kd[i] = a;
     vd[i] = b;
   }
-  if (k_scale != nullptr && blockIdx.y == 0) {
+  if (src_ks != nullptr && blockIdx.y == 0) {
     for (int hh = threadIdx.x; hh < Hkv; hh += blockDim.x) {
-      k_scale[static_cast<size_t>(dst) * Hkv + hh] = k_scale[static_cast<size_t>(src) * Hkv + hh];
-      v_scale[static_cast<size_t>(dst) * Hkv + hh] = v_scale[static_cast<size_t>(src) * Hkv + hh];
+      dst_ks[static_cast<size_t>(dst) * Hkv + hh] = src_ks[static_cast<size_t>(src) * Hkv + hh];
+      dst_vs[static_cast<size_t>(dst) * Hkv + hh] = src_vs[static_cast<size_t>(src) * Hkv + hh];
     }
   }
 }
@@ -186,19 +191,44 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
   return hipGetLastError();
 }
 
+// Chunks per block: about 8 16-byte copies per thread and cache, at most 64 work-groups a block.
+static int copy_chunks(size_t block_bytes) {
+  const size_t n16 = block_bytes / 16;
+  const int chunks = static_cast<int>((n16 + 2047) / 2048);
+  return chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks);
+}
+
+static size_t block_bytes_of(int Hkv, int D, int B, int cache_dt) {
+  const int eb = cache_dt == DT_F32 ? 4 : (cache_dt == DT_FP8 ? 1 : 2);
+  return static_cast<size_t>(Hkv) * B * D * eb;
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               const int32_t* pairs, int num_pairs, int Hkv, int D, int B, int NB,
                               int cache_dt, hipStream_t st) {
-  const int eb = cache_dt == DT_F32 ? 4 : (cache_dt == DT_FP8 ? 1 : 2);
-  const size_t block_bytes = static_cast<size_t>(Hkv) * B * D * eb;
-  const size_t n16 = block_bytes / 16;
-  int chunks = static_cast<int>((n16 + 2047) / 2048);  // ~8 16-byte copies per thread and cache
-  chunks = chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks);
+  const size_t block_bytes = block_bytes_of(Hkv, D, B, cache_dt);
   const bool fp8 = cache_dt == DT_FP8;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, chunks), dim3(256), 0, st,
-                     reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
-                     fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, pairs, NB, Hkv,
+  uint8_t* k = reinterpret_cast<uint8_t*>(k_cache);
+  uint8_t* v = reinterpret_cast<uint8_t*>(v_cache);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
+                     st, k, v, k, v, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
+                     fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, pairs, NB, NB, Hkv,
                      block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const float* src_ks, const float* src_vs, float* dst_ks,
+                              float* dst_vs, const int32_t* pairs, int num_pairs, int src_nb,
+                              int dst_nb, int Hkv, int D, int B, int cache_dt, hipStream_t st) {
+  const size_t block_bytes = block_bytes_of(Hkv, D, B, cache_dt);
+  const bool fp8 = cache_dt == DT_FP8;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
+                     st, reinterpret_cast<const uint8_t*>(src_k),
+                     reinterpret_cast<const uint8_t*>(src_v), reinterpret_cast<uint8_t*>(dst_k),
+                     reinterpret_cast<uint8_t*>(dst_v), fp8 ? src_ks : nullptr,
+                     fp8 ? src_vs : nullptr, fp8 ? dst_ks : nullptr, fp8 ? dst_vs : nullptr, pairs,
+                     src_nb, dst_nb, Hkv, block_bytes);
   return hipGetLastError();
 }
 

@@ -42,12 +42,13 @@ bool block_size_ok(int b) { return b == 8 || b == 16 || b == 32; }
 struct EventPair {
   hipEvent_t start, stop;
 };
+constexpr int kKinds = PA_KERNEL_SWAP_BLOCKS + 1;
 struct Profiler {
   bool on = false;
-  std::vector<EventPair> pending[5];
+  std::vector<EventPair> pending[kKinds];
   std::vector<EventPair> pool;
-  double ms[5] = {0, 0, 0, 0, 0};
-  long long count[5] = {0, 0, 0, 0, 0};
+  double ms[kKinds] = {};
+  long long count[kKinds] = {};
 };
 Profiler& prof() {
   static Profiler p;
@@ -73,6 +74,36 @@ void end_event(bool active, hipStream_t st, const EventPair& ev, int kind) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Pointer kinds, from the runtime's own records. A pointer the runtime does not know (pageable
+// host memory, a stale address) makes hipPointerGetAttributes fail; that error is cleared so it
+// cannot surface at a later call.
+bool pointer_kind(const void* p, hipPointerAttribute_t* attr) {
+  if (hipPointerGetAttributes(attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
+bool is_device_memory(const void* p) {
+  hipPointerAttribute_t attr;
+  return pointer_kind(p, &attr) && attr.type == hipMemoryTypeDevice;
+}
+
+// Pinned host memory: its address for kernels of the current device.
+bool pinned_device_address(void* p, void** dev) {
+  hipPointerAttribute_t attr;
+  if (!pointer_kind(p, &attr) || attr.type != hipMemoryTypeHost) return false;
+  if (hipHostGetDevicePointer(dev, p, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return *dev != nullptr;
+}
+bool pinned_device_address(const void* p, void** dev) {
+  return pinned_device_address(const_cast<void*>(p), dev);
+}
 
 // Partition plan shared by workspace sizing and the launch.
 struct Plan {
@@ -182,6 +213,60 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                                               num_pairs, num_kv_heads, head_dim, block_size,
                                               num_blocks, cache_dtype, st);
   end_event(timed, st, ev, PA_KERNEL_COPY_BLOCKS);
+  return hip_status(e);
+}
+
+int pa_swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int num_blocks,
+                   void* host_k, void* host_v, float* host_k_scale, float* host_v_scale,
+                   int num_host_blocks, const int32_t* block_pairs, int num_pairs, int direction,
+                   int num_kv_heads, int head_dim, int block_size, pa_dtype cache_dtype,
+                   void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || num_host_blocks <= 0 ||
+      head_dim <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  const bool fp8 = cache_dtype == PA_FP8_E4M3;
+  if (!k_cache || !v_cache || !host_k || !host_v || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (fp8 && (!k_scale || !v_scale || !host_k_scale || !host_v_scale)) return PA_ERR_INVALID_ARG;
+  // Device-side addresses of the pinned host pool; nothing is launched unless every pointer is of
+  // the kind the kernel can access.
+  void* dk = nullptr;
+  void* dv = nullptr;
+  void* dks = nullptr;
+  void* dvs = nullptr;
+  if (!is_device_memory(k_cache) || !is_device_memory(v_cache) ||
+      (fp8 && (!is_device_memory(k_scale) || !is_device_memory(v_scale))))
+    return PA_ERR_INVALID_ARG;
+  if (!pinned_device_address(host_k, &dk) || !pinned_device_address(host_v, &dv) ||
+      (fp8 && (!pinned_device_address(host_k_scale, &dks) ||
+               !pinned_device_address(host_v_scale, &dvs))))
+    return PA_ERR_INVALID_ARG;
+  const void* pairs = block_pairs;
+  if (!is_device_memory(block_pairs)) {
+    void* dp = nullptr;
+    if (!pinned_device_address(block_pairs, &dp)) return PA_ERR_INVALID_ARG;
+    pairs = dp;
+  }
+  const bool out = direction == PA_SWAP_OUT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  const bool timed = begin_event(st, &ev);
+  const hipError_t e =
+      out ? pa::launch_swap_blocks(k_cache, v_cache, dk, dv, k_scale, v_scale,
+                                   static_cast<float*>(dks), static_cast<float*>(dvs),
+                                   static_cast<const int32_t*>(pairs), num_pairs, num_blocks,
+                                   num_host_blocks, num_kv_heads, head_dim, block_size,
+                                   cache_dtype, st)
+          : pa::launch_swap_blocks(dk, dv, k_cache, v_cache, static_cast<const float*>(dks),
+                                   static_cast<const float*>(dvs), k_scale, v_scale,
+                                   static_cast<const int32_t*>(pairs), num_pairs, num_host_blocks,
+                                   num_blocks, num_kv_heads, head_dim, block_size, cache_dtype,
+                                   st);
+  end_event(timed, st, ev, PA_KERNEL_SWAP_BLOCKS);
   return hip_status(e);
 }
 
@@ -336,7 +421,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
 int pa_profile_enable(int on) {
   Profiler& P = prof();
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < kKinds; ++k) {
     for (const EventPair& ev : P.pending[k]) P.pool.push_back(ev);
     P.pending[k].clear();
     P.ms[k] = 0.0;
@@ -347,7 +432,7 @@ int pa_profile_enable(int on) {
 }
 
 int pa_profile_read(int kernel_kind, double* total_ms, long long* launches) {
-  if (kernel_kind < 0 || kernel_kind > 4 || !total_ms || !launches) return PA_ERR_INVALID_ARG;
+  if (kernel_kind < 0 || kernel_kind >= kKinds || !total_ms || !launches) return PA_ERR_INVALID_ARG;
   Profiler& P = prof();
   for (const EventPair& ev : P.pending[kernel_kind]) {
     if (hipEventSynchronize(ev.stop) != hipSuccess) return PA_ERR_HIP;

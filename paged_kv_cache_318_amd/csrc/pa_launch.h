@@ -26,6 +26,10 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               const int32_t* pairs, int num_pairs, int num_kv_heads,
                               int head_dim, int block_size, int num_blocks, int cache_dt,
                               hipStream_t st);
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const float* src_ks, const float* src_vs, float* dst_ks,
+                              float* dst_vs, const int32_t* pairs, int num_pairs, int src_nb,
+                              int dst_nb, int Hkv, int D, int B, int cache_dt, hipStream_t st);
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* tables, const int32_t* lens, int num_seqs,
                             int num_kv_heads, int head_dim, int block_size, int max_blocks,

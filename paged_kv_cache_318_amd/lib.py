@@ -16,7 +16,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_BLOCKS = 1
 PA_KERNEL_DECODE_PARTITION, PA_KERNEL_DECODE_MERGE, PA_KERNEL_WRITE_KV, PA_KERNEL_COPY_BLOCKS, \
-    PA_KERNEL_GATHER_KV = range(5)
+    PA_KERNEL_GATHER_KV, PA_KERNEL_SWAP_BLOCKS = range(6)
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
           -4: "PA_ERR_HIP"}
 
@@ -37,6 +38,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                    _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                        _i32, _i32, _i32, _vp], _i32),
     "pa_diag_read_bandwidth": ([_vp, _sz, _vp, _i32, _i32, _vp, _vp], _i32),
     "pa_profile_enable": ([_i32], _i32),
     "pa_profile_read": ([_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong)],
@@ -134,6 +137,39 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None, st
     _check("pa_copy_blocks", load().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_pairs) if n else None, n, Hkv, D, B, NB, dtype_code(k_cache), _stream(stream)))
+
+
+def _host_ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("host pools passed to pa_swap_blocks must be pinned host tensors")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpagedattn must be contiguous")
+    return t.data_ptr()
+
+
+def pa_swap_blocks(k_cache, v_cache, host_k, host_v, block_pairs, direction: int, k_scale=None,
+                   v_scale=None, host_k_scale=None, host_v_scale=None, stream=None) -> None:
+    """Device pool <-> pinned host pool of the same block shape. ``block_pairs`` int32 [n][2] =
+    (src, dst) on the GPU or in pinned host memory; PA_SWAP_OUT copies device block src to host
+    block dst, PA_SWAP_IN host block src to device block dst."""
+    import torch
+    NB, Hkv, B, D = k_cache.shape
+    NH = host_k.shape[0]
+    _need(tuple(host_k.shape[1:]) == (Hkv, B, D) and tuple(host_v.shape) == (NH, Hkv, D, B),
+          "host pools must be keys [num_host_blocks][Hkv][B][D], values [num_host_blocks][Hkv][D][B]")
+    _need(host_k.dtype == k_cache.dtype and host_v.dtype == v_cache.dtype, "host pool dtype differs")
+    _need(block_pairs.dtype == torch.int32 and block_pairs.dim() == 2 and block_pairs.shape[1] == 2,
+          "block_pairs must be int32 [n][2]")
+    n = block_pairs.shape[0]
+    pairs = None
+    if n:
+        pairs = _ptr(block_pairs) if block_pairs.is_cuda else _host_ptr(block_pairs)
+    _check("pa_swap_blocks", load().pa_swap_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), NB, _host_ptr(host_k),
+        _host_ptr(host_v), _host_ptr(host_k_scale), _host_ptr(host_v_scale), NH, pairs, n,
+        direction, Hkv, D, B, dtype_code(k_cache), _stream(stream)))
 
 
 def pa_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, context_lens, stream=None) -> None:

@@ -45,7 +45,7 @@ def test_diag_rejects_bad_arguments(L):
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_gather_kv",
+    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_gather_kv", "pa_swap_blocks",
               "pa_decode_workspace_bytes", "pa_status_string"):
         assert n in names
 
@@ -141,6 +141,28 @@ def _copy(L, **kw):
 ])
 def test_copy_blocks_rejects_bad_arguments(L, kw, want):
     assert _copy(L, **kw) == want
+
+
+def _swap(L, **kw):
+    a = dict(kc=FAKE, vc=FAKE, ks=None, vs=None, NB=64, hk=FAKE, hv=FAKE, hks=None, hvs=None, NH=32,
+             pairs=FAKE, n=3, dir=0, Hkv=2, D=128, B=16, cdt=F16)
+    a.update(kw)
+    return L.pa_swap_blocks(a["kc"], a["vc"], a["ks"], a["vs"], a["NB"], a["hk"], a["hv"], a["hks"],
+                            a["hvs"], a["NH"], a["pairs"], a["n"], a["dir"], a["Hkv"], a["D"], a["B"],
+                            a["cdt"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(n=-1), INVALID), (dict(NH=0), INVALID), (dict(dir=2), INVALID), (dict(dir=-1), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(B=4), UNSUPPORTED), (dict(cdt=7), INVALID),
+    (dict(hk=None), INVALID), (dict(pairs=None), INVALID), (dict(cdt=FP8), INVALID),
+    (dict(cdt=FP8, ks=FAKE, vs=FAKE), INVALID), (dict(NB=1 << 28), INVALID),
+    (dict(n=0, pairs=None, kc=None, hk=None), OK),
+])
+def test_swap_blocks_rejects_bad_arguments(L, kw, want):
+    """Scalar and null-pointer checks (all before any HIP call); the pointer-kind checks need the
+    runtime and are covered by the GPU tests."""
+    assert _swap(L, **kw) == want
 
 
 def test_gather_rejects_bad_arguments(L):

@@ -96,18 +96,86 @@ def test_block_table_padding_and_lens():
     assert p.context_lens([0, 1]).tolist() == [1, 9]
 
 
+def test_swap_out_and_in_keeps_sharing_inside_the_group():
+    """Preemption by swapping (podcast transcript, paragraph on preemption): the whole group moves
+    to host blocks, one per distinct device block, refcounts carried; the swap back takes device
+    blocks from the front of the free list and restores the same sharing."""
+    p = BlockPool(16, 4, num_host_blocks=8)
+    p.add_sequence(0, 6)                        # blocks [0, 1]
+    p.fork(0, 1)                                # shares both
+    p.append_slot(1)                            # CoW: 1 gets block 2, a copy of block 1
+    p.add_sequence(2, 3)                        # unrelated: block 3
+    out = p.swap_out([0, 1])
+    assert [d for d, _ in out] == [0, 1, 2] and len({h for _, h in out}) == 3
+    assert p.ref[0] == p.ref[1] == p.ref[2] == 0 and set(p.free) >= {0, 1, 2}
+    assert p.tables[2] == [3]
+    h = dict(out)
+    assert p.swapped[0] == [h[0], h[1]] and p.swapped[1] == [h[0], h[2]]
+    assert p.host_ref[h[0]] == 2 and p.host_ref[h[1]] == 1
+    p.check()
+    with pytest.raises(KeyError):
+        p.append_slot(0)                        # a swapped-out sequence cannot run
+    back = p.swap_in([1, 0])
+    dev = dict(back)
+    assert p.tables[0] == [dev[h[0]], dev[h[1]]] and p.tables[1] == [dev[h[0]], dev[h[2]]]
+    assert p.ref[dev[h[0]]] == 2 and len(p.host_free) == 8
+    p.check()
+
+
+def test_swap_rejects_groups_sharing_with_outsiders_and_short_pools():
+    p = BlockPool(8, 4, num_host_blocks=2)
+    p.add_sequence(0, 8)
+    p.fork(0, 1)
+    with pytest.raises(ValueError):
+        p.swap_out([0])                         # 1 still reads 0's blocks
+    p.add_sequence(2, 12)                       # three blocks
+    state = (list(p.free), list(p.ref), list(p.host_free), list(p.host_ref))
+    with pytest.raises(OutOfBlocks):
+        p.swap_out([2])                         # host pool holds two
+    assert state == (list(p.free), list(p.ref), list(p.host_free), list(p.host_ref))
+    p.swap_out([0, 1])
+    p.add_sequence(3, 20)                       # device pool now too short for the group
+    with pytest.raises(OutOfBlocks):
+        p.swap_in([0, 1])
+    p.free_sequence(0)                          # a swapped-out sequence can be dropped
+    p.check()
+    p.free_sequence(1)
+    assert len(p.host_free) == 2
+    p.check()
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_operations_keep_invariants(seed):
     """Seeded random fork / append / free sequences: invariants hold after every operation, the
     written block always has refcount 1, and freeing everything returns the whole pool."""
     rng = np.random.default_rng(seed)
     B = int(rng.choice([1, 2, 4, 16]))
-    p = BlockPool(64, B, free_order=rng.permutation(64).tolist())
-    live, nxt = [], 0
+    p = BlockPool(64, B, free_order=rng.permutation(64).tolist(), num_host_blocks=32)
+    live, nxt, out = [], 0, []
     for _ in range(400):
-        op = rng.integers(0, 10)
+        op = rng.integers(0, 12)
         try:
-            if op == 0 or not live:
+            if op == 10 and live:               # swap out a sequence with its whole sharing group
+                s0 = live[int(rng.integers(len(live)))]
+                group = {s0}
+                while True:
+                    blocks = {b for s in group for b in p.tables[s]}
+                    more = {s for s in live if s not in group and blocks & set(p.tables[s])}
+                    if not more:
+                        break
+                    group |= more
+                p.swap_out(sorted(group))
+                live = [s for s in live if s not in group]
+                out.append(sorted(group))
+            elif op == 11 and out:
+                g = out.pop(int(rng.integers(len(out))))
+                try:
+                    p.swap_in(g)
+                    live += g
+                except OutOfBlocks:
+                    out.append(g)
+                    raise
+            elif op == 0 or not live:
                 p.add_sequence(nxt, int(rng.integers(0, 3 * B)))
                 live.append(nxt)
                 nxt += 1
@@ -130,7 +198,8 @@ def test_random_operations_keep_invariants(seed):
         except OutOfBlocks:
             pass
         p.check()
-    for s in live:
+    for s in live + [s for g in out for s in g]:
         p.free_sequence(s)
     assert len(p.free) == 64 and sum(p.ref) == 0
+    assert len(p.host_free) == 32 and sum(p.host_ref) == 0
     p.check()

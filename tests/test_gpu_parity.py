@@ -404,6 +404,146 @@ def test_copy_blocks_bit_exact(dt):
         assert np.array_equal(d.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
 
 
+def _pinned_like(arr: np.ndarray, dt: str):
+    """A pinned host tensor holding ``arr`` (bf16 given as uint16 bit patterns)."""
+    src = torch.from_numpy(np.ascontiguousarray(arr))
+    if dt == "bf16":
+        src = src.view(torch.int16).view(torch.bfloat16)
+    t = torch.empty(src.shape, dtype=src.dtype, pin_memory=True)
+    t.copy_(src)
+    return t
+
+
+def _host_np(t, dt):
+    return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("pairs_on", ["device", "pinned"])
+def test_swap_blocks_round_trip_bit_exact(dt, pairs_on):
+    """Blocks go out to a pinned host pool and come back into other device blocks, bit for bit
+    (scales included for fp8); untouched blocks of either pool keep their bytes, and a pair naming
+    a block outside its pool is skipped."""
+    w = make_workload([40, 77, 130], num_heads=8, num_kv_heads=8, head_dim=128, dtype=dt, seed=41,
+                      free_fraction=1.0)
+    d = upload(w)
+    NB, NH = w.num_blocks, 24
+    rng = np.random.default_rng(6)
+    hk0 = rng.integers(0, 256, size=(NH,) + w.k_pool.shape[1:] + (w.k_pool.itemsize,),
+                       dtype=np.uint8).view(w.k_pool.dtype).reshape((NH,) + w.k_pool.shape[1:])
+    hv0 = rng.integers(0, 256, size=(NH,) + w.v_pool.shape[1:] + (w.v_pool.itemsize,),
+                       dtype=np.uint8).view(w.v_pool.dtype).reshape((NH,) + w.v_pool.shape[1:])
+    hk, hv = _pinned_like(hk0, dt), _pinned_like(hv0, dt)
+    hks = hvs = None
+    if dt == "fp8":
+        hks0 = rng.random((NH, w.k_pool.shape[1]), dtype=np.float32)
+        hvs0 = rng.random((NH, w.k_pool.shape[1]), dtype=np.float32)
+        hks, hvs = _pinned_like(hks0, "f32"), _pinned_like(hvs0, "f32")
+    perm, hperm = rng.permutation(NB), rng.permutation(NH - 1)
+    out_pairs = np.stack([perm[:12], hperm[:12]], axis=1).astype(np.int32)
+    out_pairs = np.concatenate([out_pairs, [[NB + 5, NH - 1]]]).astype(np.int32)
+    in_pairs = np.stack([hperm[:12], perm[12:24]], axis=1).astype(np.int32)
+
+    def pairs_t(a):
+        t = torch.from_numpy(a)
+        return t.cuda() if pairs_on == "device" else _pinned_like(a, "f32").view(torch.int32)
+
+    lib.pa_swap_blocks(d.k_cache, d.v_cache, hk, hv, pairs_t(out_pairs), lib.PA_SWAP_OUT,
+                       d.k_scale, d.v_scale, hks, hvs)
+    torch.cuda.synchronize()
+    ok_, ov_ = hk0.copy(), hv0.copy()
+    oks = None if hks is None else hks0.copy()
+    ovs = None if hvs is None else hvs0.copy()
+    oracle.swap_blocks(w.k_pool, w.v_pool, ok_, ov_, out_pairs, w.k_scale, w.v_scale, oks, ovs)
+    assert np.array_equal(_host_np(hk, dt).view(np.uint8), ok_.view(np.uint8))
+    assert np.array_equal(_host_np(hv, dt).view(np.uint8), ov_.view(np.uint8))
+    if oks is not None:
+        assert np.array_equal(hks.numpy().view(np.uint32), oks.view(np.uint32))
+        assert np.array_equal(hvs.numpy().view(np.uint32), ovs.view(np.uint32))
+
+    lib.pa_swap_blocks(d.k_cache, d.v_cache, hk, hv, pairs_t(in_pairs), lib.PA_SWAP_IN,
+                       d.k_scale, d.v_scale, hks, hvs)
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    ks = None if w.k_scale is None else w.k_scale.copy()
+    vs = None if w.v_scale is None else w.v_scale.copy()
+    oracle.swap_blocks(ok_, ov_, kp, vp, in_pairs, oks, ovs, ks, vs)
+    assert np.array_equal(_pool_np(d.k_cache, dt).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_pool_np(d.v_cache, dt).view(np.uint8), vp.view(np.uint8))
+    if ks is not None:
+        assert np.array_equal(d.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(d.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_decode_after_swap_out_and_in_is_bit_identical(variant):
+    """A preempted sequence resumed in other device blocks attends exactly as before: the output
+    depends on logical positions only, not on where the blocks sit."""
+    w = make_workload([40, 777, 130, 5], num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                      seed=43, free_fraction=1.0)
+    _, d = run_gpu(w, out_dt="f32", variant=variant, return_pools=True)
+
+    def decode(tables):
+        out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch.float32, device="cuda")
+        ws = workspace_for(d.q, d.k_cache, tables, w.block_size)
+        lib.pa_decode(out, d.q, d.k_cache, d.v_cache, tables, d.lens, w.scale, variant=variant,
+                      workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    before = decode(d.tables)
+    s, nb = 1, -(-777 // w.block_size)
+    mine = w.tables[s, :nb].astype(np.int32)
+    used = set(np.concatenate([w.tables[i, : -(-int(L) // w.block_size)] for i, L in enumerate(w.lens)]).tolist())
+    spare = np.array([b for b in range(w.num_blocks) if b not in used][:nb], dtype=np.int32)
+    assert spare.size == nb
+    hk = torch.empty((nb,) + tuple(d.k_cache.shape[1:]), dtype=d.k_cache.dtype, pin_memory=True)
+    hv = torch.empty((nb,) + tuple(d.v_cache.shape[1:]), dtype=d.v_cache.dtype, pin_memory=True)
+    idx = np.arange(nb, dtype=np.int32)
+    lib.pa_swap_blocks(d.k_cache, d.v_cache, hk, hv, torch.from_numpy(np.stack([mine, idx], 1)).cuda(),
+                       lib.PA_SWAP_OUT)
+    blk = torch.from_numpy(mine.astype(np.int64)).cuda()
+    d.k_cache[blk] = float("nan")             # the freed blocks are reused by someone else
+    d.v_cache[blk] = float("nan")
+    lib.pa_swap_blocks(d.k_cache, d.v_cache, hk, hv, torch.from_numpy(np.stack([idx, spare], 1)).cuda(),
+                       lib.PA_SWAP_IN)
+    tables = d.tables.clone()
+    tables[s, :nb] = torch.from_numpy(spare).cuda()
+    after = decode(tables)
+    assert np.array_equal(before, after)
+
+
+def test_swap_rejects_memory_the_kernel_cannot_reach():
+    """Pageable host memory, or device memory in place of the host pool (and the reverse), is
+    refused before any launch; a valid call right after still works."""
+    w = make_workload([40, 77], num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16", seed=45,
+                      free_fraction=1.0)
+    d = upload(w)
+    L = lib.load()
+    NB, Hkv, B, D = d.k_cache.shape
+    pageable = np.zeros((4, Hkv, B, D), np.float16)
+    pinned = _pinned_like(pageable, "f16")
+    b0 = int(w.tables[0][0])                  # a block that holds keys and values
+    pairs = torch.tensor([[b0, 1]], dtype=torch.int32, device="cuda")
+    pairs_pageable = np.array([[b0, 1]], np.int32)
+
+    def call(dk, dv, hk, hv, pr):
+        return L.pa_swap_blocks(dk, dv, None, None, NB, hk, hv, None, None, 4, pr, 1,
+                                lib.PA_SWAP_OUT, Hkv, D, B, lib.PA_F16, None)
+
+    dk, dv = d.k_cache.data_ptr(), d.v_cache.data_ptr()
+    pg = pageable.ctypes.data
+    assert call(dk, dv, pg, pg, pairs.data_ptr()) == -1                        # pageable host pool
+    assert call(dk, dv, dk, dv, pairs.data_ptr()) == -1                        # device as host pool
+    assert call(pinned.data_ptr(), dv, pinned.data_ptr(), pinned.data_ptr(), pairs.data_ptr()) == -1
+    assert call(dk, dv, pinned.data_ptr(), pinned.data_ptr(), pairs_pageable.ctypes.data) == -1
+    pinned_v = _pinned_like(pageable, "f16")
+    assert call(dk, dv, pinned.data_ptr(), pinned_v.data_ptr(), pairs.data_ptr()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(pinned.numpy()[1].view(np.uint16).ravel(), w.k_pool[b0].view(np.uint16).ravel())
+    assert np.array_equal(pinned_v.numpy()[1].view(np.uint16).ravel(), w.v_pool[b0].view(np.uint16).ravel())
+
+
 @pytest.mark.parametrize("dt,B", [("f16", 16), ("fp8", 32), ("f32", 8)])
 def test_gather_kv_bit_exact(dt, B):
     w = make_workload([1, 16, 17, 90, 0], num_heads=4, num_kv_heads=4, head_dim=64, block_size=B,

@@ -341,6 +341,59 @@ def test_copy_blocks_copies_whole_blocks_and_scales():
     assert np.array_equal(kp[others], w.k_pool[others])
 
 
+@pytest.mark.parametrize("dt", ["fp8", "bf16"])
+def test_swap_round_trip_restores_every_sequence(dt):
+    """Preemption by swapping (podcast transcript, paragraph on preemption): a group's blocks go to
+    a host pool, the device blocks are reused and overwritten, and the group comes back into other
+    device blocks. Every sequence then reads back (through its new table) exactly the keys, values
+    and scales it had; the sequences that stayed on the device are untouched. Pairs naming a block
+    outside either pool are skipped."""
+    w = _small(dt, lens=(20, 30, 9, 17), hq=2, hkv=2, D=8, B=8)
+    NB = w.num_blocks
+    pool = BlockPool(NB + 8, w.block_size, num_host_blocks=16)
+    tabs = {s: pool.add_sequence(s, int(w.lens[s])) for s in range(w.num_seqs)}
+    # the device pool in the manager's numbering: sequence s's logical block j at tabs[s][j]
+    kp = np.zeros((NB + 8,) + w.k_pool.shape[1:], w.k_pool.dtype)
+    vp = np.zeros((NB + 8,) + w.v_pool.shape[1:], w.v_pool.dtype)
+    ks = np.ones((NB + 8, w.k_pool.shape[1]), np.float32) if dt == "fp8" else None
+    vs = np.ones_like(ks) if dt == "fp8" else None
+    want = {}
+    for s in range(w.num_seqs):
+        nb = -(-int(w.lens[s]) // w.block_size)
+        for j in range(nb):
+            src = int(w.tables[s][j])
+            kp[tabs[s][j]], vp[tabs[s][j]] = w.k_pool[src], w.v_pool[src]
+            if ks is not None:
+                ks[tabs[s][j]], vs[tabs[s][j]] = w.k_scale[src], w.v_scale[src]
+        want[s] = oracle.gather_sequence(kp, vp, tabs[s], int(w.lens[s]), w.block_size)
+    want_scales = {s: None if ks is None else (ks[tabs[s]].copy(), vs[tabs[s]].copy())
+                   for s in range(w.num_seqs)}
+    hk = np.zeros((16,) + kp.shape[1:], kp.dtype)
+    hv = np.zeros((16,) + vp.shape[1:], vp.dtype)
+    hks = np.zeros((16, kp.shape[1]), np.float32) if ks is not None else None
+    hvs = np.zeros_like(hks) if ks is not None else None
+    out_pairs = pool.swap_out([1, 3])
+    oracle.swap_blocks(kp, vp, hk, hv, out_pairs + [(0, 99), (-1, 0)], ks, vs, hks, hvs)
+    freed = [d for d, _ in out_pairs]
+    kp[freed] = 0                                   # the freed device blocks are reused
+    vp[freed] = 0
+    before_resident = {s: oracle.gather_sequence(kp, vp, pool.tables[s], int(w.lens[s]), w.block_size)
+                       for s in (0, 2)}
+    pool.add_sequence(9, 3 * w.block_size)          # someone else takes blocks meanwhile
+    in_pairs = pool.swap_in([3, 1])
+    oracle.swap_blocks(hk, hv, kp, vp, in_pairs + [(16, 0)], hks, hvs, ks, vs)
+    pool.check()
+    for s in range(w.num_seqs):
+        got = oracle.gather_sequence(kp, vp, pool.tables[s], int(w.lens[s]), w.block_size)
+        np.testing.assert_array_equal(got[0], want[s][0])
+        np.testing.assert_array_equal(got[1], want[s][1])
+        if ks is not None:
+            np.testing.assert_array_equal(ks[pool.tables[s]], want_scales[s][0])
+            np.testing.assert_array_equal(vs[pool.tables[s]], want_scales[s][1])
+    for s in (0, 2):
+        np.testing.assert_array_equal(before_resident[s][0], want[s][0])
+
+
 def test_shared_prefix_logical_content_after_cow():
     """After the step's copies and writes every sample reads prompt + its own tokens + the new
     token through its table; no sample sees another sample's private tokens."""

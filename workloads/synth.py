@@ -29,7 +29,7 @@ import numpy as np
 from paged_kv_cache_318_amd.blocks import BlockPool
 
 __all__ = ["Workload", "STORAGE", "ELEM_BYTES", "round_to", "make_workload", "make_shared_prefix",
-           "config", "CONFIG_NAMES"]
+           "config", "config_lens", "CONFIG_NAMES"]
 
 STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
@@ -196,11 +196,16 @@ def make_workload(lens, *, num_heads: int, num_kv_heads: int, head_dim: int, blo
                   poison: str = "nan", table_width: Optional[int] = None,
                   scale: Optional[float] = None, name: str = "custom",
                   lens_rng: Optional[np.random.Generator] = None,
-                  placement_seed: Optional[int] = None) -> Workload:
+                  placement_seed: Optional[int] = None, placement: str = "scattered") -> Workload:
     """Independent sequences with the given attended lengths (each >= 0; a length-0 sequence gets
     no new token). The pool holds ``num_blocks`` blocks (default: blocks in use + ``free_fraction``)
     handed out in a seeded random order. ``placement_seed`` draws that order from its own generator,
-    so two workloads differing only in it hold the same logical data at different physical blocks."""
+    so two workloads differing only in it hold the same logical data at different physical blocks.
+    ``placement="contiguous"`` hands the blocks out in address order instead (every sequence's
+    blocks consecutive, sequences one after another: the layout of a contiguous cache, still read
+    through the tables); the random order is drawn all the same, so the data is the same."""
+    if placement not in ("scattered", "contiguous"):
+        raise ValueError(f"placement must be 'scattered' or 'contiguous', not {placement!r}")
     rng = lens_rng if lens_rng is not None else np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     S = lens.shape[0]
@@ -213,6 +218,8 @@ def make_workload(lens, *, num_heads: int, num_kv_heads: int, head_dim: int, blo
     if NB < used:
         raise ValueError(f"pool of {NB} blocks cannot hold {used} blocks")
     perm = (rng if placement_seed is None else np.random.default_rng(placement_seed)).permutation(NB)
+    if placement == "contiguous":
+        perm = np.arange(NB)
     pool = BlockPool(NB, B, free_order=perm.tolist())
     slots = np.full(S, -1, dtype=np.int32)
     for s in range(S):
@@ -356,6 +363,31 @@ def make_shared_prefix(*, seed: int = 4, num_prompts: int = 16, samples: int = 4
                           "decoded": d.tolist(), "samples": samples})
 
 
+def _draw_lens(n: int, rng: np.random.Generator, over: dict) -> np.ndarray:
+    """Context lengths of configurations 2, 3 and 5 (the first draws of their generators)."""
+    if n == 2:
+        S = over.pop("num_seqs", 64)
+        return rng.integers(over.pop("min_len", 128), over.pop("max_len", 2048), endpoint=True, size=S)
+    if n == 3:
+        S = over.pop("num_seqs", 128)
+        lo, hi = over.pop("clip", (64, 8192))
+        return np.clip(np.round(np.exp(rng.normal(math.log(1024.0), 1.0, size=S))), lo, hi).astype(np.int64)
+    if n == 5:
+        S = over.pop("num_seqs", 16)
+        return rng.integers(over.pop("min_len", 16384), over.pop("max_len", 32768), endpoint=True, size=S)
+    raise ValueError(f"config {n} has no drawn lengths")
+
+
+def config_lens(n: int) -> dict:
+    """Shape of configuration 2, 3 or 5 without its data: the same lengths ``config(n)`` draws,
+    head counts, head size, cache dtype and name (for timing inputs generated elsewhere)."""
+    lens = _draw_lens(n, np.random.default_rng(n), {})
+    shape = {2: (40, 40, "f16", "cfg2-opt13b-mha-f16"), 3: (32, 8, "bf16", "cfg3-gqa-long-bf16"),
+             5: (32, 8, "fp8", "cfg5-fp8-kv")}[n]
+    return {"lens": [int(x) for x in lens], "num_heads": shape[0], "num_kv_heads": shape[1],
+            "head_dim": 128, "dtype": shape[2], "name": shape[3]}
+
+
 def config(n: int, **over) -> Workload:
     """The five decode-step configurations (full size by default; keyword overrides shrink them
     for quick tests, e.g. ``num_seqs=8``)."""
@@ -368,21 +400,18 @@ def config(n: int, **over) -> Workload:
     if n == 2:
         seed = over.pop("seed", 2)
         rng = np.random.default_rng(seed)
-        S = over.pop("num_seqs", 64)
-        lens = rng.integers(over.pop("min_len", 128), over.pop("max_len", 2048), endpoint=True, size=S)
+        lens = _draw_lens(2, rng, over)
         dt = over.pop("dtype", "f16")
-        return make_workload(lens, num_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
-                             dtype=dt, seed=seed, poison=poison, lens_rng=rng,
-                             name=f"cfg2-opt13b-mha-{dt}", **over)
+        return make_workload(lens, num_heads=40, num_kv_heads=40, head_dim=128,
+                             block_size=over.pop("block_size", 16), dtype=dt, seed=seed,
+                             poison=poison, lens_rng=rng, name=f"cfg2-opt13b-mha-{dt}", **over)
     if n == 3:
         seed = over.pop("seed", 3)
         rng = np.random.default_rng(seed)
-        S = over.pop("num_seqs", 128)
-        lo, hi = over.pop("clip", (64, 8192))
-        lens = np.clip(np.round(np.exp(rng.normal(math.log(1024.0), 1.0, size=S))), lo, hi).astype(np.int64)
-        return make_workload(lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
-                             dtype=over.pop("dtype", "bf16"), seed=seed, poison=poison, lens_rng=rng,
-                             name="cfg3-gqa-long-bf16", **over)
+        lens = _draw_lens(3, rng, over)
+        return make_workload(lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=over.pop("block_size", 16), dtype=over.pop("dtype", "bf16"),
+                             seed=seed, poison=poison, lens_rng=rng, name="cfg3-gqa-long-bf16", **over)
     if n == 4:
         return make_shared_prefix(seed=over.pop("seed", 4), poison=poison,
                                   name="cfg4-shared-prefix-bf16" + ("-first-step" if over.get("first_step") else ""),
@@ -390,8 +419,7 @@ def config(n: int, **over) -> Workload:
     if n == 5:
         seed = over.pop("seed", 5)
         rng = np.random.default_rng(seed)
-        S = over.pop("num_seqs", 16)
-        lens = rng.integers(over.pop("min_len", 16384), over.pop("max_len", 32768), endpoint=True, size=S)
+        lens = _draw_lens(5, rng, over)
         return make_workload(lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                              dtype="fp8", q_dtype=over.pop("q_dtype", "bf16"), seed=seed,
                              poison=poison, lens_rng=rng, name="cfg5-fp8-kv", **over)
