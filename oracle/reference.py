@@ -51,7 +51,7 @@ __all__ = [
     "E4M3_VALUES", "e4m3_decode", "e4m3_encode", "fp8_quantize",
     "to_f64", "write_kv", "copy_blocks", "swap_blocks", "gather_sequence", "sequence_kv",
     "attention_contiguous", "attention_blockwise", "attention_split",
-    "decode", "decode_blockwise", "decode_split",
+    "decode", "decode_blockwise", "decode_split", "prefill",
     "kv_bytes_per_token", "unused_slots",
 ]
 
@@ -348,6 +348,45 @@ def decode_split(q, k_pool, v_pool, tables, lens, block_size, scale, dtype, part
 # Memory arithmetic: transcript paragraph on OPT-13B (≈800 KB per token, ≈1.6 GB per 2048
 # tokens); glossary "ページングの仕組み" (only the last block of a sequence is partly empty).
 # --------------------------------------------------------------------------------------------
+
+
+# --------------------------------------------------------------------------------------------
+# Several new query tokens per sequence (prefill of a chunk over the cached context) --
+# Wikipedia, "Математическая формулировка": the equations hold for any query position i, each
+# query attending the keys up to and including its own position.
+# --------------------------------------------------------------------------------------------
+
+
+def prefill(q, k_pool, v_pool, tables, lens, query_start, block_size, scale, dtype, q_dtype=None,
+            k_scale=None, v_scale=None, tokens=None):
+    """Causal paged attention of a chunk of new tokens per sequence. Sequence s owns query rows
+    ``query_start[s] .. query_start[s+1]-1`` (n_s of them) and attends ``lens[s]`` cached tokens,
+    the last n_s of which are its new tokens; query k (0-based) sits at position
+    ``p = lens[s] - n_s + k`` and attends positions 0..p through the table
+    (``attention_contiguous`` over the first p+1 gathered tokens). Returns float64 ``[T][Hq][D]``;
+    with ``tokens`` only those rows are computed (the rest stay zero)."""
+    q64 = to_f64(q, q_dtype or dtype)
+    T, Hq, D = q64.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    want = None if tokens is None else set(int(t) for t in tokens)
+    for s in range(qs.shape[0] - 1):
+        n = int(qs[s + 1] - qs[s])
+        if n == 0 or (want is not None and not any(qs[s] <= t < qs[s + 1] for t in want)):
+            continue
+        L = int(lens[s])
+        K, V = sequence_kv(k_pool, v_pool, tables[s], L, block_size, dtype, k_scale, v_scale)
+        for k in range(n):
+            t = int(qs[s]) + k
+            if want is not None and t not in want:
+                continue
+            p = L - n + k
+            for h in range(Hq):
+                g = h // G
+                out[t, h] = attention_contiguous(q64[t, h], K[:p + 1, g, :], V[:p + 1, g, :], scale)
+    return out
 
 
 def kv_bytes_per_token(layers, heads, head_dim, elem_bytes):

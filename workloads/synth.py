@@ -29,7 +29,7 @@ import numpy as np
 from paged_kv_cache_318_amd.blocks import BlockPool
 
 __all__ = ["Workload", "STORAGE", "ELEM_BYTES", "round_to", "make_workload", "make_shared_prefix",
-           "config", "config_lens", "CONFIG_NAMES"]
+           "config", "config_lens", "CONFIG_NAMES", "PrefillWorkload", "make_prefill"]
 
 STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
@@ -154,6 +154,134 @@ class Workload:
         if self.dtype == "fp8":
             blk += 2 * self.num_kv_heads * 4
         return int(self.cow.shape[0]) * 2 * blk
+
+
+@dataclass
+class PrefillWorkload(Workload):
+    """Host arrays of one chunked-prefill step: every sequence appends a chunk of new tokens to
+    its cached context and attends causally. ``q``, ``k_new``, ``v_new`` and ``slots`` have one
+    row per new token (T in all), sequence s owning rows ``query_start[s] .. query_start[s+1]-1``;
+    ``lens`` counts the context plus the chunk."""
+    query_start: Optional[np.ndarray] = None     # int32 [S+1]
+
+    @property
+    def new_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    def query_positions(self) -> np.ndarray:
+        """Absolute position of every query row (its own cache position)."""
+        pos = np.empty(self.new_tokens, dtype=np.int64)
+        for s in range(self.num_seqs):
+            a, b = int(self.query_start[s]), int(self.query_start[s + 1])
+            pos[a:b] = int(self.lens[s]) - (b - a) + np.arange(b - a)
+        return pos
+
+    def attended_pairs(self) -> int:
+        """(query, key) pairs the causal mask keeps: sum over query rows of position + 1."""
+        return int((self.query_positions() + 1).sum())
+
+    def prefill_flops(self) -> float:
+        """Algorithmic flops: 2 D per pair for the scores and 2 D for the weighted values, per
+        query head."""
+        return 4.0 * self.head_dim * self.num_heads * self.attended_pairs()
+
+    def prefill_bytes(self) -> int:
+        """Algorithmic bytes: every cached K/V element read once, q in and out once each."""
+        qo = 2 * self.new_tokens * self.num_heads * self.head_dim * ELEM_BYTES[self.q_dtype]
+        nb = int(sum(-(-int(L) // self.block_size) for L in self.lens))
+        return self.kv_bytes() + qo + 4 * nb + 8 * self.num_seqs
+
+
+def make_prefill(context_lens, new_lens, *, num_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int = 16, dtype: str = "bf16", q_dtype: Optional[str] = None,
+                 seed: int = 0, free_fraction: float = 0.2, poison: str = "nan",
+                 name: str = "prefill") -> PrefillWorkload:
+    """Sequences with ``context_lens[s]`` cached tokens each receive ``new_lens[s]`` new tokens
+    (their slots reserved token by token through the block manager, blocks handed out in a seeded
+    random order). fp8 caches: a block opened by the chunk gets its scales from the amax of the
+    chunk's tokens that land in it; a block already holding context keeps its scales."""
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in context_lens]
+    new = [int(x) for x in new_lens]
+    if len(ctx) != len(new) or min(ctx + new, default=0) < 0:
+        raise ValueError("context_lens and new_lens must be equally long and non-negative")
+    S, B, Hq, Hkv, D = len(ctx), block_size, num_heads, num_kv_heads, head_dim
+    q_dtype = q_dtype or (dtype if dtype != "fp8" else "bf16")
+    new_dtype = q_dtype if dtype == "fp8" else dtype
+    lens = np.array([c + n for c, n in zip(ctx, new)], dtype=np.int64)
+    used = int(sum(-(-int(L) // B) for L in lens))
+    NB = max(1, math.ceil((1.0 + free_fraction) * used))
+    pool = BlockPool(NB, B, free_order=rng.permutation(NB).tolist())
+    T = int(sum(new))
+    slots = np.empty(T, dtype=np.int32)
+    qs = np.zeros(S + 1, dtype=np.int32)
+    t = 0
+    for s in range(S):
+        pool.add_sequence(s, ctx[s])
+        for _ in range(new[s]):
+            slots[t], cow = pool.append_slot(s)
+            assert cow is None
+            t += 1
+        qs[s + 1] = t
+    W = max(max((len(pool.tables[s]) for s in range(S)), default=1), 1)
+    tables = pool.block_table(list(range(S)), width=W)
+
+    q = round_to(rng.standard_normal((T, Hq, D), dtype=np.float32), q_dtype)
+    C = int(sum(ctx))
+    Kf = rng.standard_normal((C, Hkv, D), dtype=np.float32)
+    Vf = rng.standard_normal((C, Hkv, D), dtype=np.float32)
+    kn_f = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    vn_f = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+
+    st = STORAGE[dtype]
+    k_pool = np.empty((NB, Hkv, B, D), dtype=st)
+    v_pool = np.empty((NB, Hkv, D, B), dtype=st)
+    _poison_fill(k_pool, dtype, poison, rng)
+    _poison_fill(v_pool, dtype, poison, rng)
+    k_scale = v_scale = None
+    if dtype == "fp8":
+        k_scale = np.full((NB, Hkv), np.nan, dtype=np.float32)
+        v_scale = np.full((NB, Hkv), np.nan, dtype=np.float32)
+    off = 0
+    for s in range(S):
+        n = ctx[s]
+        Ks, Vs = Kf[off:off + n], Vf[off:off + n]
+        off += n
+        if n == 0:
+            continue
+        if dtype == "fp8":
+            nb = -(-n // B)
+            kc, ksc = _quantize_sequence(Ks, nb, B)
+            vc, vsc = _quantize_sequence(Vs, nb, B)
+            _place(k_pool, v_pool, pool.tables[s], kc, vc, B)
+            for j in range(nb):
+                k_scale[pool.tables[s][j]] = ksc[j]
+                v_scale[pool.tables[s][j]] = vsc[j]
+        else:
+            _place(k_pool, v_pool, pool.tables[s], round_to(Ks, dtype), round_to(Vs, dtype), B)
+    k_new = round_to(kn_f, new_dtype)
+    v_new = round_to(vn_f, new_dtype)
+    if dtype == "fp8":
+        from_bits = lambda a: (a.astype(np.uint32) << 16).view(np.float32) if new_dtype == "bf16" \
+            else a.astype(np.float32)
+        kx, vx = from_bits(k_new), from_bits(v_new)
+        opened = {}
+        for t in range(T):
+            b = int(slots[t]) // B
+            if np.isnan(k_scale[b, 0]) or b in opened:
+                opened.setdefault(b, []).append(t)
+        for b, rows in opened.items():
+            for arr, x in ((k_scale, kx), (v_scale, vx)):
+                a = np.abs(x[rows]).max(axis=(0, 2)) / np.float32(448.0)
+                a[a == 0] = 1.0
+                arr[b] = a.astype(np.float32)
+    return PrefillWorkload(name=name, num_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                           num_blocks=NB, dtype=dtype, q_dtype=q_dtype,
+                           scale=float(1.0 / math.sqrt(D)), q=q, k_pool=k_pool, v_pool=v_pool,
+                           k_scale=k_scale, v_scale=v_scale, tables=tables,
+                           lens=lens.astype(np.int32), k_new=k_new, v_new=v_new, slots=slots,
+                           cow=np.zeros((0, 2), dtype=np.int32), unique_tokens=int(lens.sum()),
+                           meta={"seed": seed, "poison": poison}, query_start=qs)
 
 
 def _quantize_sequence(Kf: np.ndarray, nb: int, B: int):
