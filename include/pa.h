@@ -174,6 +174,31 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill -- causal paged attention of a chunk of new tokens per sequence, each query token
+ * attending the cached tokens up to and including its own position ([Wikipedia]
+ * "Математическая формулировка": the equations for a query at any position i, the last block cut
+ * at i). This is the step before decoding -- a prompt, or a chunk of one, over what is already
+ * cached -- and pa_decode is its one-token case.
+ *
+ *   q, out        device [num_tokens][num_heads][head_dim]; sequence s owns rows
+ *                 query_start[s] .. query_start[s+1]-1 (n_s rows, possibly 0).
+ *   query_start   device int32 [num_seqs + 1], non-decreasing, query_start[num_seqs] <= num_tokens.
+ *   context_lens  device int32 [num_seqs]: tokens cached for s *including* its n_s new ones,
+ *                 whose keys and values must already be written (pa_write_kv); query row k of s
+ *                 (0-based) sits at position context_lens[s] - n_s + k.
+ *   max_query_len host int >= every n_s (rows beyond it are not computed).
+ *   block_tables, k_cache, v_cache, scales, dtypes: as for pa_decode; block_size must be 16 and
+ *   the cache 16-bit or fp8 (matrix-core kernel). Rows of a sequence with n_s > context_lens[s]
+ *   are cut to the last context_lens[s]. num_tokens == 0 is a no-op. No workspace.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+               int num_seqs, int num_tokens, int max_query_len, int num_heads, int num_kv_heads,
+               int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+               pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+               const float* k_scale, const float* v_scale, void* stream);
+
+/*
  * pa_swap_blocks -- move whole blocks between the device pool and a host pool in pinned memory,
  * to preempt a group of sequences and resume it later ("vLLM и PagedAttention" (podcast
  * transcript), paragraph on preemption: a group's KV data can be moved to CPU memory and brought
@@ -212,7 +237,8 @@ typedef enum {
   PA_KERNEL_WRITE_KV = 2,
   PA_KERNEL_COPY_BLOCKS = 3,
   PA_KERNEL_GATHER_KV = 4,
-  PA_KERNEL_SWAP_BLOCKS = 5
+  PA_KERNEL_SWAP_BLOCKS = 5,
+  PA_KERNEL_PREFILL = 6
 } pa_kernel_kind;
 
 int pa_profile_enable(int on);  /* also resets the counters */

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["pa_api.cpp", "kv_ops.hip", "decode_valu.hip", "decode_mfma.hip", "diag.hip"]
+SOURCES = ["pa_api.cpp", "kv_ops.hip", "decode_valu.hip", "decode_mfma.hip", "prefill_mfma.hip",
+           "diag.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

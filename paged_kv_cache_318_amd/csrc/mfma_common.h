@@ -1,0 +1,59 @@
+// gfx950 building blocks shared by the matrix-core attention kernels: the 16x16x32 16-bit MFMA,
+// exact OCP E4M3 -> 16-bit conversion, fp32 <-> 16-bit rounding, the dim layout of the score
+// operands, and the direct global -> LDS load.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+template <int QDT>
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (QDT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two OCP E4M3 codes (bytes 0-1 of `w`, or 2-3 when HI) -> two packed 16-bit values of the
+// MFMA input type, with gfx950's scaled converter at scale 1.0: one instruction, exact (every
+// E4M3 value is representable in bf16 and fp16).
+template <int QDT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to16(uint32_t w) {
+  if constexpr (QDT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+template <int QDT>
+__device__ __forceinline__ uint32_t to16(float x) {
+  if constexpr (QDT == DT_BF16) return f32_to_bf16_rne(x);
+  else return f32_to_f16_rne(x);
+}
+template <int QDT>
+__device__ __forceinline__ float from16(uint32_t b) {
+  if constexpr (QDT == DT_BF16) return bf16_bits_to_f32(b);
+  else return f16_bits_to_f32(b);
+}
+
+// First of the 8 contiguous dims lane group q4 contributes to score MFMA kk: 16-bit keys load
+// 16 bytes (8 dims) per MFMA at byte 64*kk + 16*q4 of the row; fp8 keys load 16 bytes (16 dims,
+// two MFMAs) at byte 64*(kk/2) + 16*q4.
+template <int EB>
+__device__ __forceinline__ constexpr int dim_base(int q4, int kk) {
+  return EB == 2 ? 32 * kk + 8 * q4 : 64 * (kk / 2) + 16 * q4 + 8 * (kk % 2);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// gfx950 direct global -> LDS load: each lane's 16 bytes at `src` land at lds_base + 16 * lane.
+template <int AUX>
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_base, 16, 0, AUX);
+}
+
+}  // namespace pa

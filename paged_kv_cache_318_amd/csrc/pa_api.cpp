@@ -42,7 +42,7 @@ bool block_size_ok(int b) { return b == 8 || b == 16 || b == 32; }
 struct EventPair {
   hipEvent_t start, stop;
 };
-constexpr int kKinds = PA_KERNEL_SWAP_BLOCKS + 1;
+constexpr int kKinds = PA_KERNEL_PREFILL + 1;
 struct Profiler {
   bool on = false;
   std::vector<EventPair> pending[kKinds];
@@ -416,6 +416,59 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     e = pa::launch_decode_merge(a, head_dim, block_size, st);
     end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);
   }
+  return hip_status(e);
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+               int num_seqs, int num_tokens, int max_query_len, int num_heads, int num_kv_heads,
+               int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+               pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+               const float* k_scale, const float* v_scale, void* stream) {
+  if (num_seqs <= 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (max_query_len <= 0) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || block_size != 16) return PA_ERR_UNSUPPORTED;
+  const bool pair_ok = ((cache_dtype == PA_F16 || cache_dtype == PA_BF16) && q_dtype == cache_dtype) ||
+                       (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
+  if (!pair_ok) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  const int G = num_heads / num_kv_heads;
+  if ((static_cast<int64_t>(max_query_len) * G + 63) / 64 >= (int64_t{1} << 31)) return PA_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.query_start = query_start;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.out_dtype = out_dtype;
+  a.zscale = scale * pa::kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  const bool timed = begin_event(st, &ev);
+  const hipError_t e = pa::launch_prefill(a, cache_dtype, q_dtype, head_dim, max_query_len, st);
+  end_event(timed, st, ev, PA_KERNEL_PREFILL);
   return hip_status(e);
 }
 

@@ -164,4 +164,20 @@ struct DecodeArgs {
   float zscale;    // softmax scale * log2(e)
 };
 
+// Chunked prefill: sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q / out
+// ([num_tokens][num_heads][D]) and attends lens[s] cached tokens, its new tokens being the last.
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* query_start;
+  const float* k_scale;
+  const float* v_scale;
+  int num_seqs, num_tokens, num_heads, num_kv_heads, max_blocks, num_blocks, out_dtype;
+  float zscale;    // softmax scale * log2(e)
+};
+
 }  // namespace pa

@@ -16,7 +16,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_BLOCKS = 1
 PA_KERNEL_DECODE_PARTITION, PA_KERNEL_DECODE_MERGE, PA_KERNEL_WRITE_KV, PA_KERNEL_COPY_BLOCKS, \
-    PA_KERNEL_GATHER_KV, PA_KERNEL_SWAP_BLOCKS = range(6)
+    PA_KERNEL_GATHER_KV, PA_KERNEL_SWAP_BLOCKS, PA_KERNEL_PREFILL = range(7)
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
           -4: "PA_ERR_HIP"}
@@ -38,6 +38,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                    _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "pa_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                    _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                         _i32, _i32, _i32, _vp], _i32),
     "pa_diag_read_bandwidth": ([_vp, _sz, _vp, _i32, _i32, _vp, _vp], _i32),
@@ -137,6 +139,29 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, k_scale=None, v_scale=None, st
     _check("pa_copy_blocks", load().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_pairs) if n else None, n, Hkv, D, B, NB, dtype_code(k_cache), _stream(stream)))
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+               max_query_len: int, k_scale=None, v_scale=None, stream=None) -> None:
+    """``q``/``out`` [T][Hq][D]; ``query_start`` int32 [S+1] (sequence s owns rows
+    query_start[s] .. query_start[s+1]-1); ``context_lens`` counts each sequence's cached tokens
+    including its new ones; ``max_query_len`` >= every sequence's number of rows."""
+    import torch
+    T, Hq, D = q.shape
+    NB, Hkv, B, Dk = k_cache.shape
+    S, MB = block_tables.shape
+    _need(Dk == D and tuple(v_cache.shape) == (NB, Hkv, D, B), "cache shapes do not match q")
+    _need(tuple(out.shape) == (T, Hq, D), "out must be [T][Hq][D]")
+    _need(tuple(query_start.shape) == (S + 1,) and query_start.dtype == torch.int32,
+          "query_start must be int32 [S+1]")
+    _need(tuple(context_lens.shape) == (S,) and context_lens.dtype == torch.int32,
+          "context_lens must be int32 [S]")
+    _need(block_tables.dtype == torch.int32, "block_tables must be int32")
+    _check("pa_prefill", load().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), S, T, int(max_query_len), Hq, Hkv, D, B, MB, NB, float(scale),
+        dtype_code(q), dtype_code(k_cache), dtype_code(out), _ptr(k_scale), _ptr(v_scale),
+        _stream(stream)))
 
 
 def _host_ptr(t) -> Optional[int]:

@@ -45,7 +45,8 @@ def test_diag_rejects_bad_arguments(L):
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_gather_kv", "pa_swap_blocks",
+    for n in ("pa_write_kv", "pa_decode", "pa_prefill", "pa_copy_blocks", "pa_gather_kv",
+              "pa_swap_blocks",
               "pa_decode_workspace_bytes", "pa_status_string"):
         assert n in names
 
@@ -163,6 +164,29 @@ def test_swap_blocks_rejects_bad_arguments(L, kw, want):
     """Scalar and null-pointer checks (all before any HIP call); the pointer-kind checks need the
     runtime and are covered by the GPU tests."""
     assert _swap(L, **kw) == want
+
+
+def _prefill(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, qs=FAKE, S=4, T=40, mql=16,
+             Hq=8, Hkv=2, D=128, B=16, MB=8, NB=64, scale=0.1, qdt=BF16, cdt=BF16, odt=F32, ks=None,
+             vs=None)
+    a.update(kw)
+    return L.pa_prefill(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["qs"], a["S"],
+                        a["T"], a["mql"], a["Hq"], a["Hkv"], a["D"], a["B"], a["MB"], a["NB"],
+                        a["scale"], a["qdt"], a["cdt"], a["odt"], a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(S=0), INVALID), (dict(T=-1), INVALID), (dict(Hkv=3), INVALID), (dict(mql=0), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(qdt=9), INVALID), (dict(NB=1 << 27), INVALID),
+    (dict(B=8), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),
+    (dict(qdt=F16), UNSUPPORTED), (dict(odt=F16), UNSUPPORTED), (dict(cdt=FP8, qdt=FP8), UNSUPPORTED),
+    (dict(S=70000), UNSUPPORTED), (dict(qs=None), INVALID), (dict(out=None), INVALID),
+    (dict(cdt=FP8), INVALID), (dict(cdt=FP8, ks=FAKE), INVALID),
+    (dict(T=0, out=None, q=None, kc=None, vc=None, tab=None, lens=None, qs=None, mql=0), OK),
+])
+def test_prefill_rejects_bad_arguments(L, kw, want):
+    assert _prefill(L, **kw) == want
 
 
 def test_gather_rejects_bad_arguments(L):
