@@ -47,9 +47,10 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
-    p.add_argument("--measure", default="step", choices=("step", "swap", "paging"),
+    p.add_argument("--measure", default="step", choices=("step", "swap", "paging", "prefill"),
                    help="step: the decode-step line (default); swap: block swap to and from pinned "
-                        "host memory; paging: paged vs contiguous placement and block sizes")
+                        "host memory; paging: paged vs contiguous placement and block sizes; "
+                        "prefill: chunked prefill over the cache")
     return p.parse_args()
 
 
@@ -137,6 +138,71 @@ def measure_swap(args, lib, torch):
         "runtime_copy_d2h_gbs": gbs(t_d2h), "runtime_copy_h2d_gbs": gbs(t_h2d),
         "ms": {"swap_out": round(t_out, 3), "swap_in": round(t_in, 3), "copy_d2h": round(t_d2h, 3),
                "copy_h2d": round(t_h2d, 3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak, published
+
+
+def measure_prefill(args, lib, torch):
+    """Chunked prefill: 16 sequences append 512-token chunks to contexts of 0..3584 tokens (32
+    query / 8 kv heads x 128, bf16, block size 16). A step writes the chunks' K/V (pa_write_kv)
+    and runs causal attention of every new token over its sequence (pa_prefill)."""
+    import numpy as np
+
+    from workloads import make_prefill
+    from workloads.device import upload
+    rng = np.random.default_rng(15)
+    ctx = rng.integers(0, 3584, endpoint=True, size=16)
+    w = make_prefill(ctx, [512] * 16, num_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                     seed=15)
+    reps = [upload(w) for _ in range(max(1, args.replicas))]
+    qs = torch.from_numpy(np.ascontiguousarray(w.query_start, dtype=np.int32)).cuda()
+    T = w.q.shape[0]
+    out = torch.empty(T, w.num_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        d = reps[i % len(reps)]
+        lib.pa_write_kv(d.k_new, d.v_new, d.k_cache, d.v_cache, d.slots)
+        lib.pa_prefill(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, qs, w.scale, 512)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    lib.pa_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    p_ms, p_n = lib.pa_profile_read(lib.PA_KERNEL_PREFILL)
+    w_ms, w_n = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
+    lib.pa_profile_enable(False)
+    k_ms = p_ms / max(p_n, 1)
+    flops = w.prefill_flops()
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    line = {
+        "metric": "chunked prefill attention: TFLOP/s (causal pairs x 4 x head_dim x heads), new tokens/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/q, scattered blocks; no dataset)",
+        "new_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "config": {"workload": "prefill-16x512-gqa-bf16", "num_seqs": 16, "chunk": 512,
+                   "context": "U[0,3584]", "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                   "block_size": 16, "new_tokens": T, "causal_pairs": w.attended_pairs(),
+                   "flops": flops, "bytes": w.prefill_bytes()},
+        "kernels_us": {"prefill": round(1e3 * k_ms, 2),
+                       "write_kv": round(1e3 * w_ms / max(w_n, 1), 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_mfma",
+                     "bytes_gbs": round(w.prefill_bytes() / (k_ms * 1e-3) / 1e9, 1)},
     }
     print(json.dumps(line), flush=True)
 
@@ -302,6 +368,8 @@ def main():
         return measure_swap(args, lib, torch)
     if args.measure == "paging":
         return measure_paging(args, lib, torch)
+    if args.measure == "prefill":
+        return measure_prefill(args, lib, torch)
     over = {}
     if args.dtype:
         over["dtype"] = args.dtype

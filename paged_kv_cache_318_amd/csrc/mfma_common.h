@@ -39,6 +39,21 @@ __device__ __forceinline__ float from16(uint32_t b) {
   else return f16_bits_to_f32(b);
 }
 
+// Two fp32 values -> two packed 16-bit values of the MFMA input type (lo in bits 0-15), rounded
+// to nearest even by gfx950's packed converters (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int QDT>
+__device__ __forceinline__ uint32_t pack16x2(float a, float b) {
+  const f32x2 v{a, b};
+  if constexpr (QDT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+template <int QDT>
+__device__ __forceinline__ float lo16_to_f32(uint32_t w) { return from16<QDT>(w & 0xffffu); }
+template <int QDT>
+__device__ __forceinline__ float hi16_to_f32(uint32_t w) { return from16<QDT>(w >> 16); }
+
 // First of the 8 contiguous dims lane group q4 contributes to score MFMA kk: 16-bit keys load
 // 16 bytes (8 dims) per MFMA at byte 64*kk + 16*q4 of the row; fp8 keys load 16 bytes (16 dims,
 // two MFMAs) at byte 64*(kk/2) + 16*q4.

@@ -121,6 +121,19 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v, int ou
   }
 }
 
+// Stores 4 consecutive fp32 results (idx a multiple of 4) as out_dtype in one vector store.
+__device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v, int out_dtype) {
+  if (out_dtype == DT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = v;
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = out_dtype == DT_F16 ? f32_to_f16_rne(v[i]) : f32_to_bf16_rne(v[i]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) =
+        u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+
 // ---- DPP reductions inside one 16-lane row -------------------------------------------------------
 // quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (swaps the two
 // quads of each 8-lane half), row_mirror (swaps the two halves): after the four steps every lane

@@ -18,6 +18,8 @@
 // Each column carries its own causal limit (its query position); a wave's rows never leave it,
 // so no cross-wave merge is needed and no workspace either.
 
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -28,7 +30,8 @@ constexpr int kPrefillRows = 64;  // rows per work-group (4 waves x 16 MFMA colu
 
 template <int CDT, int D>
 constexpr size_t prefill_lds_bytes() {
-  return size_t{4} * 16 * D * Elem<CDT>::bytes;  // key tiles of two blocks, then value tiles
+  // two buffers, each the key tiles of two blocks followed by their value tiles
+  return size_t{2} * 4 * 16 * D * Elem<CDT>::bytes;
 }
 
 template <int CDT, int QDT, int D>
@@ -44,8 +47,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NCH = KT / 1024;             // 1 KB loads per tile
   static_assert(NCH >= 1 && KT % 1024 == 0, "tile must be a whole number of 1 KB loads");
   extern __shared__ float smem[];
-  uint8_t* kt = reinterpret_cast<uint8_t*>(smem);  // [2][KT] keys of the iteration's blocks
-  uint8_t* vt = kt + 2 * KT;                       // [2][KT] values (dim-major, as stored)
+  // [2 buffers][keys of blocks A, B][values of blocks A, B (dim-major, as stored)], KT bytes each
+  uint8_t* kt = reinterpret_cast<uint8_t*>(smem);
 
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
@@ -72,6 +75,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int k = live ? r / G : 0;
   const int hh = live ? r - k * G : 0;
   const int pos = live ? L - ns + k : 0;
+  // earliest query position among the wave's columns (0 if the wave has rows past the chunk,
+  // which attend token 0 only)
+  const int wrow = r0 + wave * 16;
+  const int wave_min_pos = wrow + 15 < rows ? L - ns + wrow / G : 0;
 
   u32x4 qop[KK];
   if (live) {
@@ -109,9 +116,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   for (int mi = 0; mi < MI; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), lsum = 0.0f;
 
+  // Iteration i covers blocks 2i and 2i+1 (the second may lie past the group's last query).
+  // Its tiles go to LDS buffer i & 1: the loads for i+1 are issued right after the barrier that
+  // opens iteration i, so they fly while iteration i computes.
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
+  const int niter = (nblk + 1) / 2;
   int tv = 0, tbase = -64;
-  for (int j0 = 0; j0 < nblk; j0 += 2) {
+  float zs_next[2], vs_next[2];
+  auto issue = [&](int it) {
+    const int j0 = 2 * it;
     if (j0 - tbase >= 64) {  // next 64 table entries into one VGPR, read back with readlane
       tbase = j0;
       tv = 0;
@@ -120,35 +133,46 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
       }
     }
-    const bool has_b = j0 + 1 < nblk;
     const int pba = __builtin_amdgcn_readlane(tv, j0 - tbase);
-    const int pbb = has_b ? __builtin_amdgcn_readlane(tv, j0 + 1 - tbase) : pba;
+    const int pbb = j0 + 1 < nblk ? __builtin_amdgcn_readlane(tv, j0 + 1 - tbase) : pba;
     const size_t offa = (static_cast<size_t>(pba) * Hkv + g) * KT;
     const size_t offb = (static_cast<size_t>(pbb) * Hkv + g) * KT;
+    uint8_t* buf = kt + (it & 1) * (4 * KT);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int t = ld_tile[i];
       const uint8_t* src = (t < 2 ? a.k_cache : a.v_cache) + ((t & 1) ? offb : offa) + ld_src[i];
-      dma16<0>(src, kt + t * KT + 1024 * ld_part[i]);  // values follow the keys: vt = kt + 2*KT
+      dma16<0>(src, buf + t * KT + 1024 * ld_part[i]);  // keys of A, B, then values of A, B
     }
-    float zs[2], vs[2];
-    zs[0] = zs[1] = a.zscale;
-    vs[0] = vs[1] = 1.0f;
+    zs_next[0] = zs_next[1] = a.zscale;
+    vs_next[0] = vs_next[1] = 1.0f;
     if constexpr (CDT == DT_FP8) {
-      zs[0] *= a.k_scale[static_cast<size_t>(pba) * Hkv + g];
-      zs[1] *= a.k_scale[static_cast<size_t>(pbb) * Hkv + g];
-      vs[0] = a.v_scale[static_cast<size_t>(pba) * Hkv + g];
-      vs[1] = a.v_scale[static_cast<size_t>(pbb) * Hkv + g];
+      zs_next[0] *= a.k_scale[static_cast<size_t>(pba) * Hkv + g];
+      zs_next[1] *= a.k_scale[static_cast<size_t>(pbb) * Hkv + g];
+      vs_next[0] = a.v_scale[static_cast<size_t>(pba) * Hkv + g];
+      vs_next[1] = a.v_scale[static_cast<size_t>(pbb) * Hkv + g];
     }
-    // this wave's loads have landed (both counters drained), then every wave's have
+  };
+  issue(0);
+  for (int it = 0; it < niter; ++it) {
+    const int j0 = 2 * it;
+    const bool has_b = j0 + 1 < nblk;
+    const float zs[2] = {zs_next[0], zs_next[1]};
+    const float vs[2] = {vs_next[0], vs_next[1]};
+    // This wave's loads for iteration it have landed (both counters drained: nothing newer is in
+    // flight); after the barrier every wave's have, and every wave is done reading the buffer the
+    // next loads go to.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (it + 1 < niter) issue(it + 1);
+    const uint8_t* kb0 = kt + (it & 1) * (4 * KT);
+    const uint8_t* vt = kb0 + 2 * KT;
 
     f32x4 zt[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* kb = kt + u * KT;
+      const uint8_t* kb = kb0 + u * KT;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
@@ -164,77 +188,92 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
-    // lane (q4, n) holds tokens t0(u) .. t0(u)+3 of block j0+u for column n
-    float z[8];
+    // Interior iterations (every token of both blocks at or before the wave's earliest query,
+    // so every token is also below L) need neither the causal nor the end-of-sequence mask.
+    const bool interior = (j0 + 2) * B - 1 <= wave_min_pos;
+    auto step = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      // lane (q4, n) holds tokens t0(u) .. t0(u)+3 of block j0+u for column n
+      float z[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t0 = (j0 + u) * B + 4 * q4;
+      for (int u = 0; u < 2; ++u) {
+        const int t0 = (j0 + u) * B + 4 * q4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        z[4 * u + i] = (t0 + i <= pos && (u == 0 || has_b)) ? zt[u][i] * zs[u] : neg_inf();
-    }
-    float tm = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) tm = fmaxf(tm, z[i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float mn = fmaxf(m, tm);  // finite: block 0 holds token 0, which every column attends
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float pz[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
-      psum += pz[i];
-    }
-    lsum = lsum * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
-
-    // weighted values over the 32 tokens of the two blocks; P^T as 16-bit hi part + remainder;
-    // slots at or beyond L (never written) get zero values
-    uint32_t hbits[8], lbits[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pv = pz[i] * (i < 4 ? vs[0] : vs[1]);
-      hbits[i] = to16<QDT>(pv);
-      lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
-    }
-    const u32x4 phi{hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16),
-                    hbits[4] | (hbits[5] << 16), hbits[6] | (hbits[7] << 16)};
-    const u32x4 plo{lbits[0] | (lbits[1] << 16), lbits[2] | (lbits[3] << 16),
-                    lbits[4] | (lbits[5] << 16), lbits[6] | (lbits[7] << 16)};
-    const int va = L - j0 * B - 4 * q4;                   // this lane group's tokens below L
-    const int vb = has_b ? L - (j0 + 1) * B - 4 * q4 : 0;
-    const uint32_t ma0 = va >= 2 ? 0xffffffffu : (va == 1 ? 0x0000ffffu : 0u);
-    const uint32_t ma1 = va >= 4 ? 0xffffffffu : (va == 3 ? 0x0000ffffu : 0u);
-    const uint32_t mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
-    const uint32_t mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int voff = ((16 * mi + n) * B + 4 * q4) * EB;
-      uint32_t a0, a1, c0, c1;
-      if constexpr (EB == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
-        const u32x2 y = *reinterpret_cast<const u32x2*>(vt + KT + voff);
-        a0 = x.x;
-        a1 = x.y;
-        c0 = y.x;
-        c1 = y.y;
-      } else {
-        const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
-        const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
-        a0 = fp8x2_to16<QDT, false>(x);
-        a1 = fp8x2_to16<QDT, true>(x);
-        c0 = fp8x2_to16<QDT, false>(y);
-        c1 = fp8x2_to16<QDT, true>(y);
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (MASKED)
+            z[4 * u + i] = (t0 + i <= pos && (u == 0 || has_b)) ? zt[u][i] * zs[u] : neg_inf();
+          else
+            z[4 * u + i] = zt[u][i] * zs[u];
+        }
       }
-      const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
-      acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
-      acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
-    }
-    __syncthreads();  // every wave is done with the staged tiles before the next loads land
+      float tm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      // The running max only moves when some column of the wave sees a larger score; the
+      // accumulators are rescaled only then (the result is the same for any common shift).
+      if (__builtin_amdgcn_ballot_w64(tm > m) != 0) {
+        const float mn = fmaxf(m, tm);  // finite: block 0 holds token 0, which every column attends
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
+        m = mn;
+      }
+      float pz[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pz[i] = __builtin_amdgcn_exp2f(z[i] - m);
+        lsum += pz[i];
+      }
+      // weighted values over the 32 tokens of the two blocks; P^T as 16-bit hi part +
+      // remainder; slots at or beyond L (never written) get zero values
+      uint32_t phw[4], plw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float vsc = i < 2 ? vs[0] : vs[1];
+        const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
+        phw[i] = pack16x2<QDT>(p0, p1);
+        plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
+      }
+      const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
+      const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};
+      uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
+      if constexpr (MASKED) {
+        const int va = L - j0 * B - 4 * q4;                   // this lane group's tokens below L
+        const int vb = has_b ? L - (j0 + 1) * B - 4 * q4 : 0;
+        ma0 = va >= 2 ? 0xffffffffu : (va == 1 ? 0x0000ffffu : 0u);
+        ma1 = va >= 4 ? 0xffffffffu : (va == 3 ? 0x0000ffffu : 0u);
+        mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
+        mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int voff = ((16 * mi + n) * B + 4 * q4) * EB;
+        uint32_t a0, a1, c0, c1;
+        if constexpr (EB == 2) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
+          const u32x2 y = *reinterpret_cast<const u32x2*>(vt + KT + voff);
+          a0 = x.x;
+          a1 = x.y;
+          c0 = y.x;
+          c1 = y.y;
+        } else {
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
+          const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
+          a0 = fp8x2_to16<QDT, false>(x);
+          a1 = fp8x2_to16<QDT, true>(x);
+          c0 = fp8x2_to16<QDT, false>(y);
+          c1 = fp8x2_to16<QDT, true>(y);
+        }
+        u32x4 vop{a0, a1, c0, c1};
+        if constexpr (MASKED) vop = u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
+        acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
+        acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
+      }
+    };
+    if (interior) step(std::false_type{});
+    else step(std::true_type{});
   }
 
   lsum += __shfl_xor(lsum, 16);
@@ -242,10 +281,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   if (live) {
     const size_t orow = (static_cast<size_t>(q0 + k) * Hq + g * G + hh) * D;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store_out(a.out, orow + 16 * mi + 4 * q4 + i, acc[mi][i] / lsum, a.out_dtype);
+    for (int mi = 0; mi < MI; ++mi) {
+      const f32x4 o{acc[mi][0] / lsum, acc[mi][1] / lsum, acc[mi][2] / lsum, acc[mi][3] / lsum};
+      store_out4(a.out, orow + 16 * mi + 4 * q4, o, a.out_dtype);
+    }
   }
 }
 
