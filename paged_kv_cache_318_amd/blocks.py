@@ -35,12 +35,13 @@ on the host and after the swap back (one host block per distinct device block, a
 
 from __future__ import annotations
 
+import hashlib
 from collections import deque
 from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["OutOfBlocks", "BlockPool"]
+__all__ = ["OutOfBlocks", "BlockPool", "CachingBlockPool", "block_hash"]
 
 
 class OutOfBlocks(RuntimeError):
@@ -250,3 +251,124 @@ class BlockPool:
         hused = {h for h in range(self.num_host_blocks) if self.host_ref[h] > 0}
         assert not (hfree & hused) and hfree | hused == set(range(self.num_host_blocks)), \
             "host pool: a block is both free and used, or neither"
+
+
+# ------------------------------------------------------------------------------------------------
+# Prefix caching across requests
+# ------------------------------------------------------------------------------------------------
+
+def block_hash(parent: bytes, tokens: Sequence[int]) -> bytes:
+    """Digest of one full block: SHA-256 over the parent block's digest and the block's token ids
+    (int64 little-endian). Chained this way a block's digest stands for the whole prefix that ends
+    with it, so equal digests mean equal prefixes, not just equal blocks."""
+    h = hashlib.sha256()
+    h.update(parent)
+    h.update(np.asarray(tokens, dtype="<i8").tobytes())
+    return h.digest()
+
+
+class CachingBlockPool(BlockPool):
+    """``BlockPool`` whose full blocks are also indexed by the hash of the prefix they end, so a
+    new request whose prompt starts with an already cached prefix reuses those blocks (one more
+    reference each) instead of recomputing and storing them.
+
+    Rules, by page title and section:
+
+    * "PagedAttention", Ultralytics glossary, section "シーケンス間でのブロック共有": hashing whole
+      blocks extends block sharing from the sequences of one request to different requests.
+    * "Paged Attention" study notes, section "Prefix Caching机制": a prefix is looked up by its
+      hash, a hit is confirmed by checking that the cached tokens really match the prompt, and
+      cached blocks carry reference counts.
+
+    Readings where the pages are open: only full blocks are hashed (a partly filled block still
+    changes); the hash chains the parent block's digest (a block stands for its whole prefix);
+    a hit is confirmed token by token (a digest collision never hands out wrong data); a cached
+    block whose last reference goes away stays cached and goes to the back of the free list, so
+    the least recently released cached block is the first one a new allocation reclaims (and
+    its hash entry is dropped then). Sharing a cached block never needs copy-on-write: only
+    partly filled blocks are ever written.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Iterable[int]] = None,
+                 num_host_blocks: int = 0):
+        super().__init__(num_blocks, block_size, free_order, num_host_blocks)
+        self.by_hash: Dict[bytes, int] = {}
+        self.block_key: Dict[int, Tuple[bytes, Tuple[int, ...]]] = {}  # block -> (hash, tokens)
+        self.hits = 0
+        self.lookups = 0
+
+    def _take(self, n: int) -> List[int]:
+        out = super()._take(n)
+        for b in out:                      # reclaiming a released cached block drops its entry
+            key = self.block_key.pop(b, None)
+            if key is not None:
+                del self.by_hash[key[0]]
+        return out
+
+    def _hashes(self, tokens: Sequence[int]) -> List[Tuple[bytes, Tuple[int, ...]]]:
+        B = self.block_size
+        out, parent = [], b""
+        for j in range(len(tokens) // B):
+            blk = tuple(int(t) for t in tokens[j * B:(j + 1) * B])
+            parent = block_hash(parent, blk)
+            out.append((parent, blk))
+        return out
+
+    def cached_prefix(self, tokens: Sequence[int]) -> List[int]:
+        """Physical blocks holding the longest cached prefix of ``tokens`` (full blocks only,
+        confirmed token by token); nothing is reserved."""
+        blocks = []
+        for h, blk in self._hashes(tokens):
+            b = self.by_hash.get(h)
+            if b is None or self.block_key[b][1] != blk:
+                break
+            blocks.append(b)
+        return blocks
+
+    def add_sequence_cached(self, seq_id: int, tokens: Sequence[int]) -> int:
+        """Start a sequence for the prompt ``tokens``: reuse the blocks of its longest cached
+        prefix, allocate the rest. Returns the number of prompt tokens already cached; the caller
+        computes and writes only tokens from there on (a chunked prefill whose context is the
+        cached prefix). On ``OutOfBlocks`` the state is unchanged. The caller must leave at least
+        one token to compute, so a fully cached prompt reuses all but its last block."""
+        if seq_id in self.tables or seq_id in self.swapped:
+            raise ValueError(f"sequence {seq_id} already exists")
+        n = len(tokens)
+        hit = self.cached_prefix(tokens)
+        if hit and len(hit) * self.block_size >= n:   # keep the last token to compute
+            hit = hit[:-1]
+        need = self.blocks_needed(n) - len(hit)
+        revive = [b for b in hit if self.ref[b] == 0]
+        if need > len(self.free) - len(revive):
+            raise OutOfBlocks(f"need {need} free blocks, have {len(self.free) - len(revive)}")
+        for b in revive:                   # released but still cached: back in use
+            self.free.remove(b)
+        for b in hit:
+            self.ref[b] += 1
+        self.tables[seq_id] = list(hit) + self._take(need)
+        self.lengths[seq_id] = n
+        self.lookups += 1
+        self.hits += 1 if hit else 0
+        return len(hit) * self.block_size
+
+    def register(self, seq_id: int, tokens: Sequence[int]) -> int:
+        """Index the sequence's full blocks (whose keys and values are written) under their
+        prefix hashes, so later prompts can reuse them. ``tokens`` are the sequence's token ids
+        so far. A prefix that is already cached under another block keeps that block. Returns
+        the number of blocks newly indexed."""
+        table = self.tables[seq_id]
+        added = 0
+        for j, (h, blk) in enumerate(self._hashes(tokens[: self.lengths[seq_id]])):
+            b = table[j]
+            if h in self.by_hash or b in self.block_key:
+                continue
+            self.by_hash[h] = b
+            self.block_key[b] = (h, blk)
+            added += 1
+        return added
+
+    def check(self) -> None:
+        super().check()
+        assert len(self.by_hash) == len(self.block_key), "hash index and block keys differ"
+        for h, b in self.by_hash.items():
+            assert self.block_key[b][0] == h, "hash index points at a block with another key"

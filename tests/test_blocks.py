@@ -10,7 +10,7 @@ allocation the free list cannot meet raises out-of-memory).
 import numpy as np
 import pytest
 
-from paged_kv_cache_318_amd.blocks import BlockPool, OutOfBlocks
+from paged_kv_cache_318_amd.blocks import BlockPool, CachingBlockPool, OutOfBlocks, block_hash
 
 
 def test_new_block_only_when_previous_full():
@@ -202,4 +202,154 @@ def test_random_operations_keep_invariants(seed):
         p.free_sequence(s)
     assert len(p.free) == 64 and sum(p.ref) == 0
     assert len(p.host_free) == 32 and sum(p.host_ref) == 0
+    p.check()
+
+
+# ------------------------------------------------------------------------------------------------
+# prefix caching across requests ("PagedAttention", Ultralytics glossary, section on sharing
+# blocks: hashing whole blocks extends sharing to different requests; "Paged Attention" study
+# notes, section on prefix caching: lookup by hash, confirm the match, reference counts)
+# ------------------------------------------------------------------------------------------------
+
+def _prompt(rng, shared, n):
+    return list(shared) + rng.integers(0, 50000, size=n).tolist()
+
+
+def test_second_request_reuses_the_full_blocks_of_a_shared_prompt():
+    rng = np.random.default_rng(0)
+    system = rng.integers(0, 50000, size=40).tolist()        # 2 full blocks of 16 + 8 tokens
+    a, b = _prompt(rng, system, 25), _prompt(rng, system, 3)
+    p = CachingBlockPool(32, 16)
+    assert p.add_sequence_cached(0, a) == 0                  # cold: everything to compute
+    assert p.register(0, a) == 4                             # 65 tokens: 4 full blocks indexed
+    cached = p.add_sequence_cached(1, b)
+    assert cached == 32                                      # the 2 full system blocks
+    assert p.tables[1][:2] == p.tables[0][:2] and p.tables[1][2] != p.tables[0][2]
+    assert p.ref[p.tables[0][0]] == 2 and p.ref[p.tables[0][2]] == 1
+    assert p.hits == 1 and p.lookups == 2
+    p.check()
+
+
+def test_hash_chains_the_prefix():
+    """The same block contents after a different prefix is a different block."""
+    B = 4
+    x, y, z = [1, 2, 3, 4], [5, 6, 7, 8], [9, 9, 9, 9]
+    assert block_hash(block_hash(b"", x), z) != block_hash(block_hash(b"", y), z)
+    p = CachingBlockPool(16, B)
+    p.add_sequence_cached(0, x + z + [1])
+    p.register(0, x + z + [1])
+    assert p.add_sequence_cached(1, y + z + [1]) == 0
+    assert p.add_sequence_cached(2, x + z + [2]) == 8
+    p.check()
+
+
+def test_a_hash_hit_is_confirmed_token_by_token(monkeypatch):
+    """Even if two different blocks had the same digest, the cached tokens are compared first."""
+    import paged_kv_cache_318_amd.blocks as blocks_mod
+    monkeypatch.setattr(blocks_mod, "block_hash", lambda parent, tokens: b"same")
+    p = CachingBlockPool(16, 4)
+    p.add_sequence_cached(0, [1, 2, 3, 4, 5])
+    p.register(0, [1, 2, 3, 4, 5])
+    assert p.add_sequence_cached(1, [9, 9, 9, 9, 5]) == 0
+    p.check()
+
+
+def test_released_cached_blocks_stay_reusable_until_reclaimed():
+    p = CachingBlockPool(6, 4)
+    prompt = list(range(13))                                 # 3 full blocks + 1 token
+    p.add_sequence_cached(0, prompt)
+    p.register(0, prompt)
+    p.free_sequence(0)                                       # all 4 blocks released
+    assert len(p.free) == 6 and len(p.by_hash) == 3
+    assert p.add_sequence_cached(1, prompt) == 12            # revived from the free list
+    assert all(p.ref[b] == 1 for b in p.tables[1])
+    p.check()
+    p.free_sequence(1)
+    p.add_sequence(2, 24)                                    # needs all 6 blocks: evicts entries
+    assert len(p.by_hash) == 0
+    p.free_sequence(2)
+    assert p.add_sequence_cached(3, prompt) == 0
+    p.check()
+
+
+def test_fully_cached_prompt_still_leaves_its_last_block_to_compute():
+    p = CachingBlockPool(16, 4)
+    prompt = list(range(8))
+    p.add_sequence_cached(0, prompt)
+    p.register(0, prompt)
+    assert p.add_sequence_cached(1, prompt) == 4
+    assert p.tables[1][0] == p.tables[0][0] and p.tables[1][1] != p.tables[0][1]
+    p.check()
+
+
+def test_out_of_blocks_with_cache_hits_leaves_state_unchanged():
+    p = CachingBlockPool(4, 4)
+    prompt = list(range(9))
+    p.add_sequence_cached(0, prompt)
+    p.register(0, prompt)
+    p.free_sequence(0)
+    state = (list(p.free), list(p.ref), dict(p.by_hash))
+    with pytest.raises(OutOfBlocks):
+        p.add_sequence_cached(1, prompt + list(range(100, 120)))   # 2 hits + 6 new > 4 blocks
+    assert state == (list(p.free), list(p.ref), dict(p.by_hash))
+    p.check()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_requests_with_prefix_caching_keep_invariants(seed):
+    """Requests drawn from a few system prompts, appended to, forked, freed and swapped at random:
+    invariants hold after every operation, every reused block holds exactly the tokens the new
+    prompt has at that position, and freeing everything returns the whole pool."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.choice([2, 4, 16]))
+    p = CachingBlockPool(96, B, free_order=rng.permutation(96).tolist(), num_host_blocks=48)
+    systems = [rng.integers(0, 9, size=int(rng.integers(0, 5 * B))).tolist() for _ in range(3)]
+    toks, live, out, nxt = {}, [], [], 0
+    content = {}                                             # physical block -> its tokens
+    for _ in range(300):
+        op = rng.integers(0, 6)
+        try:
+            if op <= 1 or not live:
+                prompt = systems[int(rng.integers(3))] + rng.integers(0, 9, size=int(rng.integers(1, 3 * B))).tolist()
+                cached = p.add_sequence_cached(nxt, prompt)
+                for j in range(cached // B):
+                    assert content[p.tables[nxt][j]] == tuple(prompt[j * B:(j + 1) * B])
+                for j in range(len(p.tables[nxt])):
+                    content[p.tables[nxt][j]] = tuple(prompt[j * B:(j + 1) * B])
+                p.register(nxt, prompt)
+                toks[nxt] = prompt
+                live.append(nxt)
+                nxt += 1
+            elif op == 2:
+                s = live[int(rng.integers(len(live)))]
+                slot, cow = p.append_slot(s)
+                toks[s] = toks[s] + [int(rng.integers(0, 9))]
+                j = (len(toks[s]) - 1) // B
+                content[slot // B] = tuple(toks[s][j * B:(j + 1) * B])
+                p.register(s, toks[s])
+            elif op == 3 and len(live) > 1:
+                p.free_sequence(live.pop(int(rng.integers(len(live)))))
+            elif op == 4:
+                s = live[int(rng.integers(len(live)))]
+                blocks = set(p.tables[s])
+                if all(p.ref[b] == 1 for b in blocks):
+                    p.swap_out([s])
+                    live.remove(s)
+                    out.append(s)
+            elif op == 5 and out:
+                s = out.pop()
+                try:
+                    p.swap_in([s])
+                    live.append(s)
+                    for j, b in enumerate(p.tables[s]):
+                        content[b] = tuple(toks[s][j * B:(j + 1) * B])
+                except OutOfBlocks:
+                    out.append(s)
+                    raise
+        except OutOfBlocks:
+            pass
+        p.check()
+    for s in live + out:
+        p.free_sequence(s)
+    assert len(p.free) == 96 and sum(p.ref) == 0 and len(p.host_free) == 48
     p.check()
