@@ -47,63 +47,141 @@ __device__ __forceinline__ float load_as_f32(const void* p, size_t i) {
   else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-// One thread per (new token, kv head, 8 consecutive dims): a 16-byte (32-byte for fp32) load of
-// the new key and value, one vector store of the key row piece, and 8 element stores down the
-// dim-major value column. grid = (num_tokens, ceil(Hkv * D / 8 / 256)).
-template <int IN_DT, int C_DT>
-__global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ k_new,
-                                                       const void* __restrict__ v_new,
-                                                       void* __restrict__ k_cache,
-                                                       void* __restrict__ v_cache,
-                                                       const int32_t* __restrict__ slots, int Hkv,
-                                                       int D, int B, int NB,
-                                                       const float* __restrict__ k_scale,
-                                                       const float* __restrict__ v_scale) {
+// One (new token, kv head, 8 consecutive dims) piece: a 16-byte (32-byte for fp32) load of the
+// new key and value, one vector store of the key row piece, and -- unless the values go through
+// the block-tile path below -- 8 element stores down the dim-major value column.
+template <int IN_DT, int C_DT, bool VALUES>
+__device__ __forceinline__ void write_piece(const void* __restrict__ k_new,
+                                            const void* __restrict__ v_new,
+                                            void* __restrict__ k_cache, void* __restrict__ v_cache,
+                                            int t, int slot, int hh, int d0, int Hkv, int D, int B,
+                                            const float* __restrict__ k_scale,
+                                            const float* __restrict__ v_scale) {
   constexpr int IEB = Elem<IN_DT>::bytes;
   constexpr int CEB = Elem<C_DT>::bytes;
   using CT = typename Store<C_DT>::T;
-  const int t = blockIdx.x;
-  const int chunk = blockIdx.y * blockDim.x + threadIdx.x;  // which 8-dim piece of the token
-  const int per_head = D / 8;
-  if (chunk >= Hkv * per_head) return;
-  const int slot = slots[t];
-  if (slot < 0 || slot >= NB * B) return;  // skipped token (or an out-of-range slot: ignored)
   const int b = slot / B, o = slot - (slot / B) * B;
-  const int hh = chunk / per_head, d0 = (chunk - hh * per_head) * 8;
   const size_t src = (static_cast<size_t>(t) * Hkv + hh) * D + d0;
   const Raw<8 * IEB> kr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(k_new) + src * IEB);
-  const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
   const size_t kdst = ((static_cast<size_t>(b) * Hkv + hh) * B + o) * D + d0;  // elements
   const size_t vdst = ((static_cast<size_t>(b) * Hkv + hh) * D + d0) * B + o;
   uint8_t* kc = reinterpret_cast<uint8_t*>(k_cache);
   CT* vc = reinterpret_cast<CT*>(v_cache);
   if constexpr (C_DT == DT_FP8) {
     const float ks = k_scale[static_cast<size_t>(b) * Hkv + hh];
-    const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
-    float kf[8], vf[8];
+    float kf[8];
     to_f32<IN_DT, 8>(kr.w, kf);
-    to_f32<IN_DT, 8>(vr.w, vf);
     uint32_t kw[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kw[e / 4] |= f32_to_e4m3(kf[e] / ks, kf[e]) << (8 * (e & 3));
-      vc[vdst + static_cast<size_t>(e) * B] = static_cast<CT>(f32_to_e4m3(vf[e] / vs, vf[e]));
-    }
+    for (int e = 0; e < 8; ++e) kw[e / 4] |= f32_to_e4m3(kf[e] / ks, kf[e]) << (8 * (e & 3));
     *reinterpret_cast<u32x2*>(kc + kdst) = u32x2{kw[0], kw[1]};
+    if constexpr (VALUES) {
+      const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
+      const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
+      float vf[8];
+      to_f32<IN_DT, 8>(vr.w, vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vc[vdst + static_cast<size_t>(e) * B] = static_cast<CT>(f32_to_e4m3(vf[e] / vs, vf[e]));
+    }
   } else {
     static_assert(IN_DT == C_DT, "a 16/32-bit cache stores the input bits");
 #pragma unroll
     for (int i = 0; i < 8 * CEB / 16; ++i)
       reinterpret_cast<u32x4*>(kc + kdst * CEB)[i] =
           u32x4{kr.w[4 * i], kr.w[4 * i + 1], kr.w[4 * i + 2], kr.w[4 * i + 3]};
+    if constexpr (VALUES) {
+      const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      CT v;
-      if constexpr (CEB == 4) v = vr.w[e];
-      else v = static_cast<CT>(vr.w[e / 2] >> (16 * (e & 1)));
-      vc[vdst + static_cast<size_t>(e) * B] = v;
+      for (int e = 0; e < 8; ++e) {
+        CT v;
+        if constexpr (CEB == 4) v = vr.w[e];
+        else v = static_cast<CT>(vr.w[e / 2] >> (16 * (e & 1)));
+        vc[vdst + static_cast<size_t>(e) * B] = v;
+      }
     }
   }
+}
+
+// One work-group per (group of B consecutive new tokens, kv head). When the group's slots are one
+// whole block in order -- the common case of a prompt or a chunk -- the values are transposed
+// through LDS and every dim row of the block's value tile is written whole (B * elem bytes,
+// 16-byte stores) instead of one element per row and token; any other group (decode tokens of
+// different sequences, the partial first and last block of a chunk, skipped tokens) writes piece
+// by piece. Keys are token rows either way. grid = (ceil(num_tokens / B), Hkv).
+template <int IN_DT, int C_DT>
+__global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ k_new,
+                                                       const void* __restrict__ v_new,
+                                                       void* __restrict__ k_cache,
+                                                       void* __restrict__ v_cache,
+                                                       const int32_t* __restrict__ slots, int T,
+                                                       int Hkv, int D, int B, int NB,
+                                                       const float* __restrict__ k_scale,
+                                                       const float* __restrict__ v_scale) {
+  constexpr int IEB = Elem<IN_DT>::bytes;
+  constexpr int CEB = Elem<C_DT>::bytes;
+  using CT = typename Store<C_DT>::T;
+  __shared__ int s_slot[32];
+  __shared__ int s_whole;
+  __shared__ __align__(16) uint8_t tile[128 * 32 * 4];  // [D][B] values of one block, cache type
+  const int t0 = blockIdx.x * B, hh = blockIdx.y, tid = threadIdx.x;
+  const int nt = T - t0 < B ? T - t0 : B;
+  if (tid < B) {
+    int sl = tid < nt ? slots[t0 + tid] : -1;
+    s_slot[tid] = (sl < 0 || sl >= NB * B) ? -1 : sl;  // skipped (or out-of-range: ignored)
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int whole = nt == B && s_slot[0] >= 0 && s_slot[0] % B == 0;
+    for (int i = 1; i < B && whole; ++i) whole = s_slot[i] == s_slot[0] + i;
+    s_whole = whole;
+  }
+  __syncthreads();
+  const int per_tok = D / 8;                 // 8-dim pieces of one token's head
+  const bool whole = s_whole != 0;
+  for (int w = tid; w < nt * per_tok; w += blockDim.x) {
+    const int i = w / per_tok, d0 = (w - i * per_tok) * 8;
+    const int sl = s_slot[i];
+    if (sl < 0) continue;
+    if (whole)
+      write_piece<IN_DT, C_DT, false>(k_new, v_new, k_cache, v_cache, t0 + i, sl, hh, d0, Hkv, D,
+                                      B, k_scale, v_scale);
+    else
+      write_piece<IN_DT, C_DT, true>(k_new, v_new, k_cache, v_cache, t0 + i, sl, hh, d0, Hkv, D,
+                                     B, k_scale, v_scale);
+  }
+  if (!whole) return;
+  // values of the whole block: token i's 8 dims d0.. land in column i of rows d0..d0+7
+  const int b = s_slot[0] / B;
+  CT* tl = reinterpret_cast<CT*>(tile);
+  float vs = 1.0f;
+  if constexpr (C_DT == DT_FP8) vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
+  for (int w = tid; w < B * per_tok; w += blockDim.x) {
+    const int i = w / per_tok, d0 = (w - i * per_tok) * 8;
+    const size_t src = (static_cast<size_t>(t0 + i) * Hkv + hh) * D + d0;
+    const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
+    if constexpr (C_DT == DT_FP8) {
+      float vf[8];
+      to_f32<IN_DT, 8>(vr.w, vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tl[(d0 + e) * B + i] = static_cast<CT>(f32_to_e4m3(vf[e] / vs, vf[e]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        CT v;
+        if constexpr (CEB == 4) v = vr.w[e];
+        else v = static_cast<CT>(vr.w[e / 2] >> (16 * (e & 1)));
+        tl[(d0 + e) * B + i] = v;
+      }
+    }
+  }
+  __syncthreads();
+  // the tile is the block's [D][B] value slab for this head: contiguous in the cache
+  const int n16 = D * B * CEB / 16;
+  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(v_cache) +
+                                        (static_cast<size_t>(b) * Hkv + hh) * D * B * CEB);
+  const u32x4* srcl = reinterpret_cast<const u32x4*>(tile);
+  for (int w = tid; w < n16; w += blockDim.x) dst[w] = srcl[w];
 }
 
 // grid.x = pair, grid.y = chunk of the block; 16-byte copies of both caches from block src of
@@ -169,11 +247,10 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
                            const int32_t* slots, int T, int Hkv, int D, int B, int NB, int in_dt,
                            int cache_dt, const float* k_scale, const float* v_scale,
                            hipStream_t st) {
-  const int chunks = Hkv * (D / 8);
-  const dim3 grid(T, (chunks + 255) / 256), block(256);
+  const dim3 grid((T + B - 1) / B, Hkv), block(256);
 #define PA_WRITE(I, C)                                                                         \
   hipLaunchKernelGGL((write_kv_kernel<I, C>), grid, block, 0, st, k_new, v_new, k_cache,       \
-                     v_cache, slots, Hkv, D, B, NB, k_scale, v_scale)
+                     v_cache, slots, T, Hkv, D, B, NB, k_scale, v_scale)
   if (cache_dt == DT_FP8) {
     if (in_dt == DT_F32) PA_WRITE(DT_F32, DT_FP8);
     else if (in_dt == DT_F16) PA_WRITE(DT_F16, DT_FP8);

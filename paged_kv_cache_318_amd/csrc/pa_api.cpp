@@ -182,6 +182,7 @@ int pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cac
   if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
   if (in_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (cache_dtype != PA_FP8_E4M3 && cache_dtype != in_dtype) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;

@@ -101,6 +101,28 @@ COMBOS = [  # cache, q, Hq, Hkv, D
 ]
 
 
+@pytest.mark.parametrize("dt,B,D", [("bf16", 16, 128), ("f16", 8, 64), ("f32", 32, 128),
+                                    ("fp8", 16, 128), ("fp8", 32, 64)])
+def test_chunk_write_bit_exact(dt, B, D):
+    """pa_write_kv of prefill chunks: whole blocks (values transposed through LDS and stored as
+    whole rows), the partial first and last blocks of each chunk, and an empty chunk -- byte for
+    byte against the oracle's write."""
+    w = make_prefill([0, 5, 40, 3 * B], [3 * B + 5, 1, 64, 2 * B], num_heads=4, num_kv_heads=4,
+                     head_dim=D, dtype=dt, block_size=B, seed=B + D)
+    _check_inputs(w)
+    d = upload(w)
+    lib.pa_write_kv(d.k_new, d.v_new, d.k_cache, d.v_cache, d.slots, d.k_scale, d.v_scale)
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, B, w.dtype, w.k_scale, w.v_scale,
+                    w.new_dtype)
+
+    def host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else t.cpu().numpy()
+    assert np.array_equal(host(d.k_cache).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(host(d.v_cache).view(np.uint8), vp.view(np.uint8))
+
+
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,D", COMBOS)
 def test_prefill_parity(cdt, qdt, hq, hkv, D):
     w = make_prefill(CTX, NEW, num_heads=hq, num_kv_heads=hkv, head_dim=D, dtype=cdt, q_dtype=qdt,
