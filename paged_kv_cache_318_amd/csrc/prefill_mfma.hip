@@ -103,7 +103,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     if (ld_tile[i] < 2) {  // keys: lane fetches chunk (lane % CPR) ^ (row % CPR) of its row
       const int row = RPI * ld_part[i] + lane / CPR;
       ld_src[i] = row * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
-    } else {               // values: plain contiguous 1 KB
+    } else if constexpr (EB == 2) {
+      // values: LDS holds each 16-row group of the [D][16] tile (512 B) as its 16-byte halves in
+      // [half][row] order, so the value-operand reads below (lane (q4, n): row n, tokens
+      // 4*q4 .. 4*q4+3) cover 512 contiguous bytes, each 8-byte piece once: no bank conflicts
+      // (the stored [row][half] order puts rows n and n+8 on the same banks)
+      const int mi = 2 * ld_part[i] + lane / 32, hf = (lane % 32) / 16, row = 16 * mi + lane % 16;
+      ld_src[i] = row * 32 + hf * 16;
+    } else {               // fp8 values: rows of 16 bytes, read without conflicts as stored
       ld_src[i] = ld_part[i] * 1024 + 16 * lane;
     }
   }
@@ -249,7 +256,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const int voff = ((16 * mi + n) * B + 4 * q4) * EB;
+        const int voff = EB == 2 ? 512 * mi + 256 * (q4 / 2) + 16 * n + 8 * (q4 % 2)
+                                 : (16 * mi + n) * B + 4 * q4;
         uint32_t a0, a1, c0, c1;
         if constexpr (EB == 2) {
           const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
