@@ -34,8 +34,11 @@ constexpr size_t prefill_lds_bytes() {
   return size_t{2} * 4 * 16 * D * Elem<CDT>::bytes;
 }
 
+// 3 wave64s per SIMD (at most 168 registers a lane); the fp8 instances at D = 128 need a few
+// more for their converted operands and run at 2 rather than spill.
 template <int CDT, int QDT, int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void prefill_mfma_kernel(
+    PrefillArgs a) {
   constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int KK = D / 32;                 // score MFMAs per block
@@ -94,24 +97,38 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 
   // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: tile c / NCH (0, 1: keys of
   // blocks A, B; 2, 3: their values), part c % NCH of it.
-  int ld_tile[NCH], ld_part[NCH], ld_src[NCH];
+  // LDS buffer: keys of blocks A and B ([2][KT], rows XOR-swizzled), then their values. 16-bit
+  // values are stored per 16-row group mi as 1 KB: [block A, B][half][row] of 16-byte halves of
+  // the stored [row][16 tokens] rows. The value-operand read of lane (q4, n) (row n, tokens
+  // 4*q4 .. 4*q4+3) then covers 512 contiguous bytes per block, each 8-byte piece once (no bank
+  // conflicts; the stored [row][half] order puts rows n and n+8 on the same banks), and its two
+  // 8-byte pieces (block A, block B) sit 512 bytes apart: one paired read fills the operand.
+  // fp8 values keep the stored [row][16 tokens] order (16-byte rows read without conflicts).
+  // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: c < 2*NCH are keys (block
+  // c / NCH, part c % NCH of its tile); the rest are values (16-bit: group mi = c - 2*NCH, lanes
+  // 0-31 block A, 32-63 block B; fp8: block (c - 2*NCH) / NCH, part (c - 2*NCH) % NCH).
+  int ld_dst[NCH], ld_src[NCH];
+  bool ld_key[NCH], ld_b[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = wave + 4 * i;
-    ld_tile[i] = c / NCH;
-    ld_part[i] = c - (c / NCH) * NCH;
-    if (ld_tile[i] < 2) {  // keys: lane fetches chunk (lane % CPR) ^ (row % CPR) of its row
-      const int row = RPI * ld_part[i] + lane / CPR;
+    ld_key[i] = c < 2 * NCH;
+    if (c < 2 * NCH) {  // keys: lane fetches chunk (lane % CPR) ^ (row % CPR) of its row
+      const int part = c % NCH;
+      const int row = RPI * part + lane / CPR;
+      ld_b[i] = c >= NCH;
       ld_src[i] = row * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
+      ld_dst[i] = (c / NCH) * KT + 1024 * part;
     } else if constexpr (EB == 2) {
-      // values: LDS holds each 16-row group of the [D][16] tile (512 B) as its 16-byte halves in
-      // [half][row] order, so the value-operand reads below (lane (q4, n): row n, tokens
-      // 4*q4 .. 4*q4+3) cover 512 contiguous bytes, each 8-byte piece once: no bank conflicts
-      // (the stored [row][half] order puts rows n and n+8 on the same banks)
-      const int mi = 2 * ld_part[i] + lane / 32, hf = (lane % 32) / 16, row = 16 * mi + lane % 16;
+      const int mi = c - 2 * NCH, hf = (lane % 32) / 16, row = 16 * mi + lane % 16;
+      ld_b[i] = lane >= 32;
       ld_src[i] = row * 32 + hf * 16;
-    } else {               // fp8 values: rows of 16 bytes, read without conflicts as stored
-      ld_src[i] = ld_part[i] * 1024 + 16 * lane;
+      ld_dst[i] = 2 * KT + 1024 * mi;
+    } else {
+      const int v = c - 2 * NCH;
+      ld_b[i] = v >= NCH;
+      ld_src[i] = (v % NCH) * 1024 + 16 * lane;
+      ld_dst[i] = 2 * KT + (v / NCH) * KT + 1024 * (v % NCH);
     }
   }
   int kread[KL];
@@ -147,9 +164,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     uint8_t* buf = kt + (it & 1) * (4 * KT);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int t = ld_tile[i];
-      const uint8_t* src = (t < 2 ? a.k_cache : a.v_cache) + ((t & 1) ? offb : offa) + ld_src[i];
-      dma16<0>(src, buf + t * KT + 1024 * ld_part[i]);  // keys of A, B, then values of A, B
+      const uint8_t* src = (ld_key[i] ? a.k_cache : a.v_cache) + (ld_b[i] ? offb : offa) + ld_src[i];
+      dma16<0>(src, buf + ld_dst[i]);
     }
     zs_next[0] = zs_next[1] = a.zscale;
     vs_next[0] = vs_next[1] = 1.0f;
@@ -254,19 +270,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
         mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
       }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int voff = EB == 2 ? 512 * mi + 256 * (q4 / 2) + 16 * n + 8 * (q4 % 2)
-                                 : (16 * mi + n) * B + 4 * q4;
+      // value operand of group mi: tokens 4*q4 .. 4*q4+3 of block A, then of block B
+      auto vop_of = [&](int mi) -> u32x4 {
         uint32_t a0, a1, c0, c1;
         if constexpr (EB == 2) {
+          const int voff = 1024 * mi + 256 * (q4 / 2) + 16 * n + 8 * (q4 % 2);
           const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
-          const u32x2 y = *reinterpret_cast<const u32x2*>(vt + KT + voff);
+          const u32x2 y = *reinterpret_cast<const u32x2*>(vt + voff + 512);
           a0 = x.x;
           a1 = x.y;
           c0 = y.x;
           c1 = y.y;
         } else {
+          const int voff = (16 * mi + n) * B + 4 * q4;
           const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
           const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
           a0 = fp8x2_to16<QDT, false>(x);
@@ -274,10 +290,21 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           c0 = fp8x2_to16<QDT, false>(y);
           c1 = fp8x2_to16<QDT, true>(y);
         }
-        u32x4 vop{a0, a1, c0, c1};
-        if constexpr (MASKED) vop = u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
-        acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
-        acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
+        if constexpr (MASKED) return u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
+        else return u32x4{a0, a1, c0, c1};
+      };
+      // groups of 4 value tiles: the hi MFMAs of the group, then its remainder MFMAs, so no MFMA
+      // waits on the one just issued into the same accumulator
+#pragma unroll
+      for (int m0 = 0; m0 < MI; m0 += 4) {
+        u32x4 vop[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vop[j] = vop_of(m0 + j);
+          acc[m0 + j] = mfma_k32<QDT>(vop[j], phi, acc[m0 + j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m0 + j] = mfma_k32<QDT>(vop[j], plo, acc[m0 + j]);
       }
     };
     if (interior) step(std::false_type{});
