@@ -174,6 +174,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- the slot write and the decode of one step in one pass: the same result, in
+ * the cache and in `out`, as pa_write_kv(k_new, v_new, ..., slot_mapping, num_tokens = num_seqs)
+ * followed by pa_decode ([Ultralytics] "ページングの仕組み": the new token goes to its slot;
+ * [Wikipedia] "Математическая формулировка": the query attends every cached token including its
+ * own), bit for bit. The new token of sequence s is its position context_lens[s] - 1: the
+ * work-group that loads that position's block puts the new key and value (fp8: quantised with the
+ * block's scale exactly as pa_write_kv stores them) into the loaded tile in its registers, and
+ * stores the key row and the block's whole value tile back, so no separate write launch precedes
+ * the attention.
+ *
+ *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim] in new_dtype: the cache dtype for a
+ *                 16/32-bit cache, q_dtype for an fp8 cache.
+ *   slot_mapping  device int32 [num_seqs]: slot of sequence s's new token; it must be the slot of
+ *                 position context_lens[s] - 1 of block_tables[s] (that block owned by s alone,
+ *                 as copy-on-write guarantees). A negative slot, or one that is not that
+ *                 position's, is skipped: nothing is written and the cache is attended as it is.
+ *   everything else as for pa_decode (same workspace size).
+ */
+int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
+                     const void* v_new, const int32_t* slot_mapping, pa_dtype new_dtype,
+                     int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                     pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                     const float* v_scale, int partition_tokens, int variant, int flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill -- causal paged attention of a chunk of new tokens per sequence, each query token
  * attending the cached tokens up to and including its own position ([Wikipedia]
  * "Математическая формулировка": the equations for a query at any position i, the last block cut

@@ -32,6 +32,7 @@
 // fp8 caches: codes are converted exactly to the MFMA input type; the per-(block, kv head) key
 // scale multiplies the scores and the value scale multiplies P, never the codes.
 
+#include "kv_write.h"
 #include "mfma_common.h"
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -78,6 +79,13 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, n = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  // pa_decode_append: the segment holding the unit's last block substitutes the new token
+  // (position L-1, offset o_new of that block) for what the cache holds there -- in the staged
+  // key tile and in the value registers -- and stores the key row and the whole value tile back
+  // (whole lines rather than one element per dim row).
+  const int nblk_all = (L + B - 1) / B;
+  const int slot_new = (a.new_slots != nullptr && b1 == nblk_all) ? new_token_slot(a, s, L, B) : -1;
+  const int o_new = (L - 1) % B;
 
   u32x4 qop[KK];
   if (n < G) {
@@ -146,6 +154,23 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
         vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + offs[u] + ((16 * mi + n) * B + 4 * q4) * EB);
+    // the new token's rows, fetched along with the tile they go into (block u_new of this
+    // iteration, if any): lane l < D/8 the key dims 8l .. 8l+7, lane (q4, n) value dims 16*mi + n
+    int u_new = -1;
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+      if (slot_new >= 0 && u < nlive && ja + 4 * u == nblk_all - 1) u_new = u;
+    u32x4 knew{0u, 0u, 0u, 0u};
+    uint32_t vnew[MI / 2];  // two 16-bit values a register
+    if (u_new >= 0) {
+      const size_t row = (static_cast<size_t>(s) * Hkv + g) * D;
+      const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new) + row;
+      const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new) + row;
+      if (lane < D / 8) knew = *reinterpret_cast<const u32x4*>(kn + 8 * lane);
+#pragma unroll
+      for (int mi = 0; mi < MI; mi += 2)
+        vnew[mi / 2] = static_cast<uint32_t>(vn[16 * mi + n]) | (static_cast<uint32_t>(vn[16 * mi + 16 + n]) << 16);
+    }
 
     float zs[NBI], vs[NBI];
 #pragma unroll
@@ -161,6 +186,47 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     // counter have drained (waiting on vmcnt alone let the reads below see stale LDS when the
     // staged tile was the last one issued), hence the full wait: vmcnt(0) lgkmcnt(0).
     __builtin_amdgcn_s_waitcnt(0);
+
+    if (u_new >= 0) {
+      int pbn = pbs[0];
+      size_t offn = offs[0];
+#pragma unroll
+      for (int u = 1; u < NBI; ++u)
+        if (u == u_new) {
+          pbn = pbs[u];
+          offn = offs[u];
+        }
+      float ks = 1.0f;
+      if constexpr (CDT == DT_FP8) ks = a.k_scale[static_cast<size_t>(pbn) * Hkv + g];
+      uint8_t* kslot = const_cast<uint8_t*>(a.k_cache) + offn + o_new * D * EB;
+      uint8_t* krow_lds = kbuf + u_new * KT + o_new * CPR * 16;
+      if (lane < D / 8) {  // key row o_new of the staged tile (XOR-swizzled) and of the cache
+        Raw<16> in;
+        in.w[0] = knew.x; in.w[1] = knew.y; in.w[2] = knew.z; in.w[3] = knew.w;
+        const Raw<8 * EB> kc = new_key_piece<CDT, QDT, 8>(in, ks);
+        if constexpr (EB == 2) {
+          store_raw<16>(krow_lds + 16 * (lane ^ (o_new % CPR)), kc);
+          store_raw<16>(kslot + 16 * lane, kc);
+        } else {
+          store_raw<8>(krow_lds + 16 * ((lane / 2) ^ (o_new % CPR)) + 8 * (lane % 2), kc);
+          store_raw<8>(kslot + 8 * lane, kc);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NBI; ++u) {  // (u == u_new: a static index keeps vr in registers)
+        if (u != u_new) continue;
+        if (o_new >= 4 * q4 && o_new < 4 * q4 + 4) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+            put_elem<EB>(vr[u][mi], o_new - 4 * q4,
+                         new_value_bits<CDT, QDT>((vnew[mi / 2] >> (16 * (mi & 1))) & 0xffffu, vs[u]));
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          store_raw<4 * EB>(const_cast<uint8_t*>(a.v_cache) + offs[u] + ((16 * mi + n) * B + 4 * q4) * EB,
+                            vr[u][mi]);
+      }
+    }
 
     // scores of the iteration's blocks
     f32x4 zt[NBI];
@@ -254,7 +320,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     }
   }
   }
-  __syncthreads();  // every wave is done with its staged key tiles: the LDS is reused below
+  lds_barrier();  // every wave is done with its staged key tiles: the LDS is reused below
 
 
   // per-column sum over the four lane groups, then merge the four waves through LDS
@@ -273,7 +339,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm_o[(wave * G + n) * D + 16 * mi + 4 * q4 + i] = acc[mi][i];
   }
-  __syncthreads();
+  lds_barrier();
   for (int idx = tid; idx < G * D; idx += 256) {
     const int nn = idx / D, d = idx - (idx / D) * D;
     float M = sm_m[nn];
@@ -295,7 +361,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
       if (d == 0) a.ws_ml[slot * G + nn] = make_float2(M, den);
     }
   }
-  __syncthreads();  // the LDS is free for the next segment
+  lds_barrier();  // the LDS is free for the next segment
 }
 
 // Fixed partitions: grid (kv head, sequence, partition); one segment per work-group.

@@ -23,6 +23,7 @@
 // Tokens at or beyond L in the last block are excluded by selects (never by multiplying by 0),
 // so whatever sits in unused slots -- NaN included -- cannot reach the output.
 
+#include "kv_write.h"
 #include "pa_device.h"
 #include "pa_launch.h"
 #include "pa_sched.h"
@@ -58,6 +59,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int b1 = min(nblk, b0 + a.part_blocks);
   const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
   const int g = h / (Hq / Hkv);
+  // pa_decode_append: the partition holding the last block substitutes the new token (position
+  // L-1, offset o_new of that block) for what the cache holds there, in the registers its tile
+  // was loaded into, and -- one work-group per kv head -- stores the key row and the whole value
+  // tile back (whole lines rather than one element per dim row).
+  constexpr int NDT = CDT == DT_FP8 ? QDT : CDT;  // dtype of the new rows
+  constexpr int NEB = Elem<NDT>::bytes;
+  const int slot_new = (a.new_slots != nullptr && b1 == nblk) ? new_token_slot(a, s, L, B) : -1;
+  const int o_new = (L - 1) % B;
+  const bool writer = h % (Hq / Hkv) == 0;
 
   // query dims c*DPL .. c*DPL+DPL-1, as fp32
   float qf[DPL];
@@ -90,6 +100,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     Raw<DPL * EB> kr[kValuBlocksPerIter][TPR];
     Raw<TPR * EB> vr[kValuBlocksPerIter][DPL];
     int pbs[kValuBlocksPerIter];
+    Raw<DPL * NEB> knew;
+    uint32_t vnew[DPL];
 #pragma unroll
     for (int u = 0; u < kValuBlocksPerIter; ++u) {
       if (it + u >= cnt) break;
@@ -105,6 +117,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int jj = 0; jj < DPL; ++jj)
         vr[u][jj] = load_raw<TPR * EB, NT>(vt + ((c + 16 * jj) * B + r * TPR) * EB);
+      if (slot_new >= 0 && b0 + wave + 4 * (base_i + it + u) == nblk - 1) {
+        // the new token's rows, fetched along with the tile they go into
+        const size_t row = (static_cast<size_t>(s) * Hkv + g) * D;
+        knew = load_raw<DPL * NEB>(reinterpret_cast<const uint8_t*>(a.k_new) + (row + c * DPL) * NEB);
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) {
+          if constexpr (NEB == 4) vnew[jj] = reinterpret_cast<const uint32_t*>(a.v_new)[row + c + 16 * jj];
+          else vnew[jj] = reinterpret_cast<const uint16_t*>(a.v_new)[row + c + 16 * jj];
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < kValuBlocksPerIter; ++u) {
@@ -118,6 +140,30 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       vs = a.v_scale[static_cast<size_t>(pb) * Hkv + g];
     }
     const int valid = L - j * B - r * TPR;  // tokens of this row below L (may be <= 0 or > TPR)
+    if (slot_new >= 0 && j == nblk - 1) {
+      float ks = 1.0f, vsc = 1.0f;
+      if constexpr (CDT == DT_FP8) {
+        ks = a.k_scale[static_cast<size_t>(pb) * Hkv + g];
+        vsc = vs;
+      }
+      const Raw<DPL * EB> kc = new_key_piece<CDT, NDT, DPL>(knew, ks);
+      const int rn = o_new / TPR, en = o_new - rn * TPR;  // row and element holding the token
+#pragma unroll
+      for (int i = 0; i < TPR; ++i)
+        if (r == rn && i == en) kr[u][i] = kc;
+      if (r == rn) {
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) put_elem<EB>(vr[u][jj], en, new_value_bits<CDT, NDT>(vnew[jj], vsc));
+      }
+      if (writer) {
+        const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
+        uint8_t* kt = const_cast<uint8_t*>(a.k_cache) + base;
+        uint8_t* vt = const_cast<uint8_t*>(a.v_cache) + base;
+        if (r == rn) store_raw<DPL * EB>(kt + (o_new * D + c * DPL) * EB, kc);
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) store_raw<TPR * EB>(vt + ((c + 16 * jj) * B + r * TPR) * EB, vr[u][jj]);
+      }
+    }
 
     float z[TPR];
 #pragma unroll
@@ -170,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int jj = 0; jj < DPL; ++jj) sm_acc[k][c + 16 * jj] = acc[jj];
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     float M = sm_m[0];
 #pragma unroll

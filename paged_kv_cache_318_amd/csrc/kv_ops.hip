@@ -9,99 +9,12 @@
 // Layouts: k_cache [NB][Hkv][B][D] (a token's key is a contiguous row of D elements),
 // v_cache [NB][Hkv][D][B] (values are dim-major inside a block), fp8 scales [NB][Hkv].
 
+#include "kv_write.h"
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-template <int DT> struct Store;
-template <> struct Store<DT_F32> { using T = uint32_t; };
-template <> struct Store<DT_F16> { using T = uint16_t; };
-template <> struct Store<DT_BF16> { using T = uint16_t; };
-template <> struct Store<DT_FP8> { using T = uint8_t; };
-
-// |y| -> OCP E4M3 magnitude code, with the sign bit taken from x (the value before division by
-// the positive block scale, so a NaN quotient cannot lose its sign): round to nearest, ties to the
-// even mantissa; |y| >= 448 (and infinity) saturates to 448; NaN -> 0x7F.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y, float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7fu;
-  const float fa = __uint_as_float(a);
-  if (fa >= 448.0f) return sign | 0x7eu;
-  if (fa < 0.015625f) {
-    // below the smallest normal 2^-6 the codes step by 2^-9: scale by 2^9 (exact) and round half
-    // to even; a result of 8 is the smallest normal's code 0x08.
-    return sign | static_cast<uint32_t>(__builtin_rintf(fa * 512.0f));
-  }
-  // keep 3 mantissa bits of the fp32 pattern, rounding half to even at bit 20; a carry moves
-  // into the exponent, which is then rebiased from 127 to 7.
-  const uint32_t rnd = a + 0x7ffffu + ((a >> 20) & 1u);
-  return sign | ((((rnd >> 23) - 120u) << 3) | ((rnd >> 20) & 7u));
-}
-
-template <int IN_DT>
-__device__ __forceinline__ float load_as_f32(const void* p, size_t i) {
-  if constexpr (IN_DT == DT_F32) return reinterpret_cast<const float*>(p)[i];
-  else if constexpr (IN_DT == DT_F16) return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-  else return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-}
-
-// One (new token, kv head, 8 consecutive dims) piece: a 16-byte (32-byte for fp32) load of the
-// new key and value, one vector store of the key row piece, and -- unless the values go through
-// the block-tile path below -- 8 element stores down the dim-major value column.
-template <int IN_DT, int C_DT, bool VALUES>
-__device__ __forceinline__ void write_piece(const void* __restrict__ k_new,
-                                            const void* __restrict__ v_new,
-                                            void* __restrict__ k_cache, void* __restrict__ v_cache,
-                                            int t, int slot, int hh, int d0, int Hkv, int D, int B,
-                                            const float* __restrict__ k_scale,
-                                            const float* __restrict__ v_scale) {
-  constexpr int IEB = Elem<IN_DT>::bytes;
-  constexpr int CEB = Elem<C_DT>::bytes;
-  using CT = typename Store<C_DT>::T;
-  const int b = slot / B, o = slot - (slot / B) * B;
-  const size_t src = (static_cast<size_t>(t) * Hkv + hh) * D + d0;
-  const Raw<8 * IEB> kr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(k_new) + src * IEB);
-  const size_t kdst = ((static_cast<size_t>(b) * Hkv + hh) * B + o) * D + d0;  // elements
-  const size_t vdst = ((static_cast<size_t>(b) * Hkv + hh) * D + d0) * B + o;
-  uint8_t* kc = reinterpret_cast<uint8_t*>(k_cache);
-  CT* vc = reinterpret_cast<CT*>(v_cache);
-  if constexpr (C_DT == DT_FP8) {
-    const float ks = k_scale[static_cast<size_t>(b) * Hkv + hh];
-    float kf[8];
-    to_f32<IN_DT, 8>(kr.w, kf);
-    uint32_t kw[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kw[e / 4] |= f32_to_e4m3(kf[e] / ks, kf[e]) << (8 * (e & 3));
-    *reinterpret_cast<u32x2*>(kc + kdst) = u32x2{kw[0], kw[1]};
-    if constexpr (VALUES) {
-      const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
-      const float vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
-      float vf[8];
-      to_f32<IN_DT, 8>(vr.w, vf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vc[vdst + static_cast<size_t>(e) * B] = static_cast<CT>(f32_to_e4m3(vf[e] / vs, vf[e]));
-    }
-  } else {
-    static_assert(IN_DT == C_DT, "a 16/32-bit cache stores the input bits");
-#pragma unroll
-    for (int i = 0; i < 8 * CEB / 16; ++i)
-      reinterpret_cast<u32x4*>(kc + kdst * CEB)[i] =
-          u32x4{kr.w[4 * i], kr.w[4 * i + 1], kr.w[4 * i + 2], kr.w[4 * i + 3]};
-    if constexpr (VALUES) {
-      const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        CT v;
-        if constexpr (CEB == 4) v = vr.w[e];
-        else v = static_cast<CT>(vr.w[e / 2] >> (16 * (e & 1)));
-        vc[vdst + static_cast<size_t>(e) * B] = v;
-      }
-    }
-  }
-}
 
 // One work-group per (group of B consecutive new tokens, kv head). When the group's slots are one
 // whole block in order -- the common case of a prompt or a chunk -- the values are transposed

@@ -317,13 +317,17 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
   return need;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-              int num_heads, int num_kv_heads, int head_dim, int block_size,
-              int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
-              pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
-              const float* v_scale, int partition_tokens, int variant, int flags,
-              void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// pa_decode, and pa_decode_append when k_new != nullptr (new tokens taken along and written).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                int num_heads, int num_kv_heads, int head_dim, int block_size,
+                int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                const float* v_scale, int partition_tokens, int variant, int flags,
+                void* workspace, size_t workspace_bytes, void* stream, const void* k_new,
+                const void* v_new, const int32_t* slot_mapping) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
@@ -404,6 +408,9 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   a.heads_per_unit = gu;
   a.balanced = balanced ? 1 : 0;
   a.nw = nw;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = k_new != nullptr ? slot_mapping : nullptr;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;
@@ -418,6 +425,39 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+              pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+              const float* v_scale, int partition_tokens, int variant, int flags,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     q_dtype, cache_dtype, out_dtype, k_scale, v_scale, partition_tokens, variant,
+                     flags, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
+                     const void* v_new, const int32_t* slot_mapping, pa_dtype new_dtype,
+                     int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                     pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                     const float* v_scale, int partition_tokens, int variant, int flags,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(new_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(q_dtype)) return PA_ERR_INVALID_ARG;
+  // the new rows are stored as they are (16/32-bit caches) or quantised from the query type (fp8)
+  if (new_dtype != (cache_dtype == PA_FP8_E4M3 ? q_dtype : cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     q_dtype, cache_dtype, out_dtype, k_scale, v_scale, partition_tokens, variant,
+                     flags, workspace, workspace_bytes, stream, k_new, v_new, slot_mapping);
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -65,6 +65,23 @@ __device__ __forceinline__ Raw<NB> load_raw(const void* p) {
   return r;
 }
 
+// Stores NB bytes (a Raw piece) at an NB-aligned address.
+template <int NB>
+__device__ __forceinline__ void store_raw(void* p, const Raw<NB>& r) {
+  if constexpr (NB == 2) {
+    *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(r.w[0]);
+  } else if constexpr (NB == 4) {
+    *reinterpret_cast<uint32_t*>(p) = r.w[0];
+  } else if constexpr (NB == 8) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{r.w[0], r.w[1]};
+  } else {
+    static_assert(NB % 16 == 0, "unsupported store width");
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i)
+      reinterpret_cast<u32x4*>(p)[i] = u32x4{r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]};
+  }
+}
+
 // ---- storage -> fp32 (all exact) -------------------------------------------------------------
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xffffu)));
@@ -100,6 +117,27 @@ __device__ __forceinline__ void to_f32(const uint32_t* w, float* f) {
   }
 }
 
+// ---- fp32 -> OCP E4M3 code (the fp8 cache write) ------------------------------------------
+// |y| -> OCP E4M3 magnitude code, with the sign bit taken from x (the value before division by
+// the positive block scale, so a NaN quotient cannot lose its sign): round to nearest, ties to the
+// even mantissa; |y| >= 448 (and infinity) saturates to 448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y, float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  const float fa = __uint_as_float(a);
+  if (fa >= 448.0f) return sign | 0x7eu;
+  if (fa < 0.015625f) {
+    // below the smallest normal 2^-6 the codes step by 2^-9: scale by 2^9 (exact) and round half
+    // to even; a result of 8 is the smallest normal's code 0x08.
+    return sign | static_cast<uint32_t>(__builtin_rintf(fa * 512.0f));
+  }
+  // keep 3 mantissa bits of the fp32 pattern, rounding half to even at bit 20; a carry moves
+  // into the exponent, which is then rebiased from 127 to 7.
+  const uint32_t rnd = a + 0x7ffffu + ((a >> 20) & 1u);
+  return sign | ((((rnd >> 23) - 120u) << 3) | ((rnd >> 20) & 7u));
+}
+
 // ---- fp32 -> 16-bit storage ---------------------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
@@ -132,6 +170,15 @@ __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v, int o
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) =
         u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   }
+}
+
+// Work-group barrier for hand-offs through LDS only: orders LDS accesses (this wave's complete
+// before the barrier) but does not wait for the wave's outstanding global stores, which nothing
+// in the work-group reads back (a store of a new token's rows into the cache, say).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---- DPP reductions inside one 16-lane row -------------------------------------------------------
@@ -175,6 +222,12 @@ struct DecodeArgs {
   int balanced;    // 1: balanced split over nw work-groups; 0: fixed partitions
   int nw;
   float zscale;    // softmax scale * log2(e)
+  // pa_decode_append: the batch's new tokens ([S][Hkv][D], the cache dtype, or the query dtype for
+  // an fp8 cache) and their slots; each kernel takes sequence s's new token from here at position
+  // L-1 and the work-group holding its block writes it into the cache. nullptr: plain decode.
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
 };
 
 // Chunked prefill: sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q / out

@@ -16,11 +16,19 @@ from . import lib
 def decode_step(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new, slot_mapping,
                 cow_pairs, scale: float, k_scale=None, v_scale=None, partition_tokens: int = 0,
                 variant: int = lib.PA_VARIANT_AUTO, workspace=None, stream=None,
-                flags: int = 0) -> None:
+                flags: int = 0, fused: bool = True) -> None:
     """All tensors on the GPU; ``cow_pairs`` is int32 [n][2] (n may be 0). ``flags`` as for
-    ``pa_decode`` (PA_DECODE_SHARED_BLOCKS when sequences of the batch share blocks)."""
+    ``pa_decode`` (PA_DECODE_SHARED_BLOCKS when sequences of the batch share blocks). With
+    ``fused`` the slot write rides along with the attention (pa_decode_append: one launch fewer,
+    the new token taken from k_new / v_new); otherwise pa_write_kv then pa_decode."""
     if cow_pairs is not None and cow_pairs.shape[0] > 0:
         lib.pa_copy_blocks(k_cache, v_cache, cow_pairs, k_scale, v_scale, stream=stream)
+    if fused:
+        lib.pa_decode_append(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                             slot_mapping, scale, k_scale, v_scale,
+                             partition_tokens=partition_tokens, variant=variant,
+                             workspace=workspace, stream=stream, flags=flags)
+        return
     lib.pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=stream)
     lib.pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
                   partition_tokens=partition_tokens, variant=variant, workspace=workspace,

@@ -45,7 +45,8 @@ def test_diag_rejects_bad_arguments(L):
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_prefill", "pa_copy_blocks", "pa_gather_kv",
+    for n in ("pa_write_kv", "pa_decode", "pa_decode_append", "pa_prefill", "pa_copy_blocks",
+              "pa_gather_kv",
               "pa_swap_blocks",
               "pa_decode_workspace_bytes", "pa_status_string"):
         assert n in names
@@ -164,6 +165,30 @@ def test_swap_blocks_rejects_bad_arguments(L, kw, want):
     """Scalar and null-pointer checks (all before any HIP call); the pointer-kind checks need the
     runtime and are covered by the GPU tests."""
     assert _swap(L, **kw) == want
+
+
+def _append(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, kn=FAKE, vn=FAKE, slots=FAKE,
+             ndt=BF16, S=4, Hq=8, Hkv=2, D=128, B=16, MB=8, NB=64, scale=0.1, qdt=BF16, cdt=BF16,
+             odt=F32, ks=None, vs=None, part=0, variant=0, flags=0, ws=None, wsb=0)
+    a.update(kw)
+    return L.pa_decode_append(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["kn"],
+                              a["vn"], a["slots"], a["ndt"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                              a["B"], a["MB"], a["NB"], a["scale"], a["qdt"], a["cdt"], a["odt"],
+                              a["ks"], a["vs"], a["part"], a["variant"], a["flags"], a["ws"],
+                              a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ndt=F16), UNSUPPORTED), (dict(ndt=FP8, cdt=FP8), UNSUPPORTED), (dict(ndt=9), INVALID),
+    (dict(cdt=FP8, ndt=FP8, ks=FAKE, vs=FAKE), UNSUPPORTED), (dict(kn=None), INVALID),
+    (dict(slots=None), INVALID), (dict(S=0), INVALID), (dict(flags=4), INVALID),
+    (dict(D=100), UNSUPPORTED), (dict(cdt=FP8, qdt=BF16, ndt=BF16), INVALID),
+])
+def test_decode_append_rejects_bad_arguments(L, kw, want):
+    """The new rows' dtype must be the cache dtype (the query dtype for an fp8 cache); every other
+    check is pa_decode's."""
+    assert _append(L, **kw) == want
 
 
 def _prefill(L, **kw):

@@ -77,7 +77,9 @@ def _check_inputs(w):
     assert np.all((w.cow >= 0) & (w.cow < NB))
 
 
-def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False, flags=0):
+def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False, flags=0, fused=True):
+    """One step through the library: copies, then the fused write + decode (pa_decode_append), or
+    with ``fused=False`` pa_write_kv then pa_decode."""
     _check_inputs(w)
     d = upload(w)
     out_dt = out_dt or w.q_dtype
@@ -85,7 +87,7 @@ def run_gpu(w, out_dt=None, part=0, variant=0, return_pools=False, flags=0):
     ws = workspace_for(d.q, d.k_cache, d.tables, w.block_size, part)
     decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
                 w.scale, d.k_scale, d.v_scale, partition_tokens=part, variant=variant, workspace=ws,
-                flags=flags)
+                flags=flags, fused=fused)
     torch.cuda.synchronize()
     res = to_numpy_f64(out)
     if return_pools:
@@ -209,6 +211,59 @@ def test_balanced_split_cuts_units(lens, cdt):
     fixed = run_gpu(w, out_dt="f32", part=512, variant=2)
     assert np.max(np.abs(got - fixed)) <= TOL[cdt]
     assert np.array_equal(got, run_gpu(w, out_dt="f32", variant=2))
+
+
+@pytest.mark.parametrize("cdt,qdt,hq,hkv,D,B,variant", COMBOS)
+@pytest.mark.parametrize("part", [0, 256])
+def test_separate_write_and_decode_parity(cdt, qdt, hq, hkv, D, B, variant, part):
+    """The unfused step (pa_write_kv, then pa_decode reading the new token back from the cache)
+    against the oracle, and against the fused step (pa_decode_append, which puts the new token
+    into the tile it loads): outputs and caches bit for bit equal."""
+    if hq // hkv > 16 and variant == 2:
+        pytest.skip("the MFMA variant takes at most 16 query heads per kv head")
+    w = make_workload(list(SMALL_LENS), num_heads=hq, num_kv_heads=hkv, head_dim=D, block_size=B,
+                      dtype=cdt, q_dtype=qdt, seed=hq * 1000 + D + B)
+    sep, ds = run_gpu(w, out_dt="f32", part=part, variant=variant, return_pools=True, fused=False)
+    fus, df = run_gpu(w, out_dt="f32", part=part, variant=variant, return_pools=True, fused=True)
+    assert_close(sep, run_oracle(w), cdt, "f32", f"separate {cdt}/{qdt} Hq={hq} Hkv={hkv} D={D} B={B}")
+    assert np.array_equal(sep, fus)
+    for a, b in ((ds.k_cache, df.k_cache), (ds.v_cache, df.v_cache)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
+def test_fused_step_skips_slots_that_are_not_the_last_position(variant, cdt):
+    """pa_decode_append with some slots negative and one that is not its sequence's last position:
+    those sequences attend the cache as it is and nothing is written for them."""
+    lens = [5, 17, 40, 100, 333, 1000]
+    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, seed=33)
+    d = upload(w)
+    slots = w.slots.copy()
+    lens2 = w.lens.copy()
+    skip = [1, 4]
+    for s_ in skip:                      # no new token: attend the L-1 tokens already cached
+        slots[s_] = -1
+        lens2[s_] -= 1
+    lens2[2] -= 1                        # slot of position L-1, but the sequence now ends at L-2
+    tables = w.tables
+    out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    ws = workspace_for(d.q, d.k_cache, d.tables, w.block_size)
+    lens_t = torch.from_numpy(lens2.astype(np.int32)).cuda()
+    lib.pa_decode_append(out, d.q, d.k_cache, d.v_cache, d.tables, lens_t, d.k_new, d.v_new,
+                         torch.from_numpy(slots).cuda(), w.scale, d.k_scale, d.v_scale,
+                         variant=variant, workspace=ws)
+    torch.cuda.synchronize()
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    ks = None if w.k_scale is None else w.k_scale.copy()
+    vs = None if w.v_scale is None else w.v_scale.copy()
+    written = slots.copy()
+    written[2] = -1
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, written, w.block_size, w.dtype, ks, vs, w.new_dtype)
+    ref = oracle.decode(w.q, kp, vp, tables, lens2, w.block_size, w.scale, w.dtype, w.q_dtype, ks, vs)
+    assert_close(to_numpy_f64(out), ref, cdt, "f32", "skipped slots")
+    assert np.array_equal(_pool_np(d.k_cache, cdt).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_pool_np(d.v_cache, cdt).view(np.uint8), vp.view(np.uint8))
 
 
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,variant", [("f16", "f16", 4, 4, 1), ("bf16", "bf16", 8, 2, 2),
@@ -565,13 +620,15 @@ def test_gather_kv_bit_exact(dt, B):
         assert not np.any(kon[s, L:].view(np.uint8))
 
 
-def test_profile_counts_launches():
+@pytest.mark.parametrize("fused", [False, True])
+def test_profile_counts_launches(fused):
+    """A step launches the attention kernel and the merge, plus the write unless it rides along."""
     w = cfg(1)
     lib.pa_profile_enable(True)
-    run_gpu(w, part=16)
+    run_gpu(w, part=16, fused=fused)
     ms, n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
     ms_m, n_m = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
     ms_w, n_w = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
     lib.pa_profile_enable(False)
-    assert (n, n_m, n_w) == (1, 1, 1)
-    assert ms > 0 and ms_m > 0 and ms_w > 0
+    assert (n, n_m, n_w) == (1, 1, 0 if fused else 1)
+    assert ms > 0 and ms_m > 0 and (fused or ms_w > 0)
