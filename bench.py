@@ -47,6 +47,11 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--fused", action="store_true",
+                   help="step through pa_decode_append (the write rides along with the attention) "
+                        "instead of pa_write_kv + pa_decode")
+    p.add_argument("--num-seqs", type=int, default=0,
+                   help="configs 2, 3, 5: use only this many sequences (a smaller batch)")
     p.add_argument("--measure", default="step", choices=("step", "swap", "paging", "prefill"),
                    help="step: the decode-step line (default); swap: block swap to and from pinned "
                         "host memory; paging: paged vs contiguous placement and block sizes; "
@@ -375,6 +380,8 @@ def main():
         over["dtype"] = args.dtype
     if args.first_step:
         over["first_step"] = True
+    if args.num_seqs > 0:
+        over["num_seqs"] = args.num_seqs
     t_gen = time.perf_counter()
     w = config(args.config, **over)
     t_gen = time.perf_counter() - t_gen
@@ -396,7 +403,7 @@ def main():
         d = reps[i % len(reps)]
         decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
-                    variant=args.variant, workspace=ws, flags=flags)
+                    variant=args.variant, workspace=ws, flags=flags, fused=args.fused)
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20)
@@ -470,6 +477,8 @@ def main():
             "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
             "replicas": args.replicas, "partition_tokens": args.partition, "variant": args.variant,
             "shared_blocks_flag": shared,
+            "write": "fused into the attention (pa_decode_append)" if args.fused
+                     else "separate launch (pa_write_kv, then pa_decode)",
         },
         "kernels_us": {
             "step_with_events": round(1e3 * ms_step_profiled, 2),
