@@ -216,7 +216,7 @@ def measure_paging(args, lib, torch):
     """The pages say the paged kernel pays for its indirection and that the block size trades
     table overhead against the unused tail. Same kernel, same lengths: blocks scattered through the
     pool vs handed out in address order (every sequence contiguous), for block sizes 8, 16 and 32,
-    on the MHA batch (VALU kernel) and the GQA batch (MFMA kernel at 16, VALU otherwise)."""
+    on the MHA batch (VALU kernel) and the GQA batch (MFMA kernel at 16 and 32, VALU at 8)."""
     from paged_kv_cache_318_amd.step import workspace_for
     from workloads.synth import config_lens
     rows = []
@@ -250,7 +250,7 @@ def measure_paging(args, lib, torch):
                 G = spec["num_heads"] // spec["num_kv_heads"]
                 rows.append({
                     "workload": spec["name"], "block_size": B, "placement": placement,
-                    "kernel": "decode_mfma" if (B == 16 and G >= 2) else "decode_valu",
+                    "kernel": "decode_mfma" if (B in (16, 32) and G >= 2) else "decode_valu",
                     "attention_us": round(us, 2),
                     "merge_us": round(1e3 * m_ms / m_n, 2) if m_n else None,
                     "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),

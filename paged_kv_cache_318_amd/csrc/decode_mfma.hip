@@ -60,19 +60,22 @@ constexpr size_t mfma_lds_bytes(int G, int S, bool balanced) {
 // One segment: blocks [b0, b1) of unit (sequence s, kv head g) -- all G query heads of the group.
 // The result is either the unit's final output (the segment covers all of it) or a partial result
 // in workspace slot `slot`. Every thread of the work-group calls it (it synchronises).
-template <int CDT, int QDT, int D, bool NT>
+template <int CDT, int QDT, int D, int B, bool NT>
 __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, int s, int g, int L,
                                              int b0, int b1, bool final_out, size_t slot) {
-  constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
-  constexpr int KK = D / 32;                 // score MFMAs per block
+  constexpr int SUB = B / 16;                // 16-token tiles per block
+  constexpr int KK = D / 32;                 // score MFMAs per tile
   constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
   constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per block
-  constexpr int KT = B * D * EB;             // bytes of one key tile
+  constexpr int KT = 16 * D * EB;            // bytes of one 16-token key tile
+  constexpr int KTB = B * D * EB;            // bytes of one (block, kv head) key or value tile
   constexpr int CPR = D * EB / 16;           // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;              // key rows per 1 KB load instruction
-  constexpr int NI = B / RPI;                // load instructions per key tile
-  constexpr int NBI = mfma_blocks_per_iter(EB);  // blocks per iteration (16 KB in flight)
+  constexpr int NI = 16 / RPI;               // load instructions per key tile
+  constexpr int NBI = mfma_blocks_per_iter(EB);  // 16-token tiles per iteration (16 KB in flight)
+  constexpr int BPI = NBI / SUB;             // blocks per iteration
+  static_assert(BPI >= 1 && NBI % SUB == 0, "an iteration takes whole blocks");
   constexpr int kKeyAux = NT ? 2 : 0;        // cache policy of the key loads (2: non-temporal)
   constexpr bool kNtV = NT;
   const int tid = threadIdx.x;
@@ -85,7 +88,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // (whole lines rather than one element per dim row).
   const int nblk_all = (L + B - 1) / B;
   const int slot_new = (a.new_slots != nullptr && b1 == nblk_all) ? new_token_slot(a, s, L, B) : -1;
-  const int o_new = (L - 1) % B;
+  const int o_new = (L - 1) % 16;            // within its 16-token tile
+  const int sub_new = ((L - 1) % B) / 16;     // which tile of its block
 
   u32x4 qop[KK];
   if (n < G) {
@@ -121,8 +125,9 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
 
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  // this wave's blocks are b0 + wave + 4*i, taken NBI per iteration; their table entries are
-  // fetched 64 at a time into one VGPR and read back with readlane
+  // this wave's blocks are b0 + wave + 4*i, taken BPI per iteration (NBI 16-token tiles: tile u
+  // is 16-token part u % SUB of block u / SUB); their table entries are fetched 64 at a time into
+  // one VGPR and read back with readlane
   const int nmine = b0 + wave < b1 ? (b1 - b0 - wave + 3) / 4 : 0;
   for (int base_i = 0; base_i < nmine; base_i += 64) {
   const int cnt = min(64, nmine - base_i);
@@ -131,19 +136,21 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     tv = trow[b0 + wave + 4 * (base_i + lane)];
     tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
   }
-  for (int it = 0; it < cnt; it += NBI) {
-    const int nlive = min(NBI, cnt - it);  // blocks of this iteration (the last may have fewer)
+  for (int it = 0; it < cnt; it += BPI) {
+    const int nlive = min(BPI, cnt - it);  // blocks of this iteration (the last may have fewer)
     const int ja = b0 + wave + 4 * (base_i + it);
     int pbs[NBI];
-    size_t offs[NBI];
+    size_t offs[NBI], voffs[NBI];  // key tile start; value tile start + the tile's token column
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
-      pbs[u] = __builtin_amdgcn_readlane(tv, it + (u < nlive ? u : 0));
-      offs[u] = (static_cast<size_t>(pbs[u]) * Hkv + g) * KT;
+      pbs[u] = __builtin_amdgcn_readlane(tv, it + (u / SUB < nlive ? u / SUB : 0));
+      const size_t bt = (static_cast<size_t>(pbs[u]) * Hkv + g) * KTB;
+      offs[u] = bt + (u % SUB) * KT;
+      voffs[u] = bt + (u % SUB) * 16 * EB;
     }
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
-      if (u >= nlive) break;
+      if (u / SUB >= nlive) break;
 #pragma unroll
       for (int ii = 0; ii < NI; ++ii)
         dma16<kKeyAux>(a.k_cache + offs[u] + dsrc[ii], kbuf + u * KT + 1024 * ii);
@@ -153,13 +160,14 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     for (int u = 0; u < NBI; ++u)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + offs[u] + ((16 * mi + n) * B + 4 * q4) * EB);
+        vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + voffs[u] + ((16 * mi + n) * B + 4 * q4) * EB);
     // the new token's rows, fetched along with the tile they go into (block u_new of this
     // iteration, if any): lane l < D/8 the key dims 8l .. 8l+7, lane (q4, n) value dims 16*mi + n
     int u_new = -1;
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
-      if (slot_new >= 0 && u < nlive && ja + 4 * u == nblk_all - 1) u_new = u;
+      if (slot_new >= 0 && u / SUB < nlive && ja + 4 * (u / SUB) == nblk_all - 1 && u % SUB == sub_new)
+        u_new = u;
     u32x4 knew{0u, 0u, 0u, 0u};
     uint32_t vnew[MI / 2];  // two 16-bit values a register
     if (u_new >= 0) {
@@ -189,7 +197,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
     if (u_new >= 0) {
       int pbn = pbs[0];
-      size_t offn = offs[0];
+      size_t offn = offs[0];  // the new token's key tile
 #pragma unroll
       for (int u = 1; u < NBI; ++u)
         if (u == u_new) {
@@ -223,7 +231,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
         }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-          store_raw<4 * EB>(const_cast<uint8_t*>(a.v_cache) + offs[u] + ((16 * mi + n) * B + 4 * q4) * EB,
+          store_raw<4 * EB>(const_cast<uint8_t*>(a.v_cache) + voffs[u] + ((16 * mi + n) * B + 4 * q4) * EB,
                             vr[u][mi]);
       }
     }
@@ -233,7 +241,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
       zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u >= nlive) continue;
+      if (u / SUB >= nlive) continue;
       const uint8_t* kb = kbuf + u * KT;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
@@ -252,7 +260,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     }
     int valid[NBI];  // this lane group's tokens below L, per block (<= 0: none)
 #pragma unroll
-    for (int u = 0; u < NBI; ++u) valid[u] = u < nlive ? L - (ja + 4 * u) * B - 4 * q4 : 0;
+    for (int u = 0; u < NBI; ++u)
+      valid[u] = u / SUB < nlive ? L - ((ja + 4 * (u / SUB)) * B + 16 * (u % SUB)) - 4 * q4 : 0;
     float z[4 * NBI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
@@ -282,7 +291,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     // Tokens at or beyond L get zero values (their weights are already 0).
 #pragma unroll
     for (int pr = 0; pr < NBI / 2; ++pr) {
-      if (2 * pr >= nlive) break;
+      if ((2 * pr) / SUB >= nlive) break;
       const int u0 = 2 * pr, u1 = 2 * pr + 1;
       uint32_t hbits[8], lbits[8];
 #pragma unroll
@@ -369,14 +378,14 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 // few tiles in flight per CU, 4 forces spills.
 // NT: non-temporal K/V loads (streaming; the default) or cached ones (blocks shared between
 // sequences of the batch).
-template <int CDT, int QDT, int D, bool NT>
+template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int Hq = a.num_heads, G = Hq / a.num_kv_heads;
   int L = a.lens[s];
-  L = L < 0 ? 0 : (L > a.max_blocks * 16 ? a.max_blocks * 16 : L);
-  const int nblk = (L + 15) / 16;
+  L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  const int nblk = (L + B - 1) / B;
   const int b0 = p * a.part_blocks;
   if (b0 >= nblk) {
     if (p == 0)
@@ -386,16 +395,15 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   }
   const int b1 = min(nblk, b0 + a.part_blocks);
   const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-  mfma_segment<CDT, QDT, D, NT>(a, smem, s, g, L, b0, b1, nparts == 1,
+  mfma_segment<CDT, QDT, D, B, NT>(a, smem, s, g, L, b0, b1, nparts == 1,
                                 (static_cast<size_t>(s) * a.num_kv_heads + g) * a.max_parts + p);
 }
 
 // Balanced split: work-group i of a.nw takes tiles [i*W/nw, (i+1)*W/nw) of the flattened
 // (sequence, kv head, block) list and walks them unit by unit.
-template <int CDT, int QDT, int D, bool NT>
+template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
-  constexpr int B = 16;
   constexpr int EB = Elem<CDT>::bytes;
   const size_t stage = mfma_lds_bytes<CDT, D>(a.num_heads / a.num_kv_heads, 0, false);
   int* lens_lds = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) + stage);
@@ -419,55 +427,59 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs
     const long long uend = t - j + nb;
     const long long seg_end = hi < uend ? hi : uend;
     const bool whole = (j == 0) && (seg_end == uend);
-    mfma_segment<CDT, QDT, D, NT>(a, smem, s, g, lens_lds[s], j, j + static_cast<int>(seg_end - t),
+    mfma_segment<CDT, QDT, D, B, NT>(a, smem, s, g, lens_lds[s], j, j + static_cast<int>(seg_end - t),
                                   whole, static_cast<size_t>(2 * i + (t == lo ? 0 : 1)));
     t = seg_end;
   }
   (void)EB;
 }
 
-template <int CDT, int QDT, int D>
-static hipError_t launch_mfma_dn(const DecodeArgs& a, hipStream_t st) {
+template <int CDT, int QDT, int D, int B>
+static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
   const size_t shm = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.balanced != 0);
   if (a.balanced) {
     const dim3 grid(a.nw);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, false>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
   } else {
     const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, false>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
   }
   return hipGetLastError();
 }
 
 template <int CDT, int QDT>
-static hipError_t launch_mfma_d(const DecodeArgs& a, int D, hipStream_t st) {
-  if (D == 64) return launch_mfma_dn<CDT, QDT, 64>(a, st);
-  if (D == 128) return launch_mfma_dn<CDT, QDT, 128>(a, st);
+static hipError_t launch_mfma_d(const DecodeArgs& a, int D, int B, hipStream_t st) {
+  if (D == 64 && B == 16) return launch_mfma_dnb<CDT, QDT, 64, 16>(a, st);
+  if (D == 64 && B == 32) return launch_mfma_dnb<CDT, QDT, 64, 32>(a, st);
+  if (D == 128 && B == 16) return launch_mfma_dnb<CDT, QDT, 128, 16>(a, st);
+  if (D == 128 && B == 32) return launch_mfma_dnb<CDT, QDT, 128, 32>(a, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, hipStream_t st) {
-  if (cdt == DT_F16 && qdt == DT_F16) return launch_mfma_d<DT_F16, DT_F16>(a, D, st);
-  if (cdt == DT_BF16 && qdt == DT_BF16) return launch_mfma_d<DT_BF16, DT_BF16>(a, D, st);
-  if (cdt == DT_FP8 && qdt == DT_F16) return launch_mfma_d<DT_FP8, DT_F16>(a, D, st);
-  if (cdt == DT_FP8 && qdt == DT_BF16) return launch_mfma_d<DT_FP8, DT_BF16>(a, D, st);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, int B, hipStream_t st) {
+  if (cdt == DT_F16 && qdt == DT_F16) return launch_mfma_d<DT_F16, DT_F16>(a, D, B, st);
+  if (cdt == DT_BF16 && qdt == DT_BF16) return launch_mfma_d<DT_BF16, DT_BF16>(a, D, B, st);
+  if (cdt == DT_FP8 && qdt == DT_F16) return launch_mfma_d<DT_FP8, DT_F16>(a, D, B, st);
+  if (cdt == DT_FP8 && qdt == DT_BF16) return launch_mfma_d<DT_FP8, DT_BF16>(a, D, B, st);
   return hipErrorInvalidValue;
 }
 
 // Work-groups per CU the balanced kernel keeps resident (from the occupancy calculator).
-int mfma_groups_per_cu(int cdt, int qdt, int D, int G, int S, bool stream_kv) {
+int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S, bool stream_kv) {
   int n = 0;
   const void* k = nullptr;
-#define PA_PICK(C, Q, DD)                                                                        \
-  if (cdt == C && qdt == Q && D == DD)                                                           \
-    k = stream_kv ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, true>)  \
-                  : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, false>);
-  PA_PICK(DT_F16, DT_F16, 64) PA_PICK(DT_F16, DT_F16, 128) PA_PICK(DT_BF16, DT_BF16, 64)
-  PA_PICK(DT_BF16, DT_BF16, 128) PA_PICK(DT_FP8, DT_F16, 64) PA_PICK(DT_FP8, DT_F16, 128)
-  PA_PICK(DT_FP8, DT_BF16, 64) PA_PICK(DT_FP8, DT_BF16, 128)
+#define PA_PICK(C, Q, DD, BB)                                                                       \
+  if (cdt == C && qdt == Q && D == DD && B == BB)                                                   \
+    k = stream_kv ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, true>) \
+                  : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, false>);
+#define PA_PICK_B(C, Q, DD) PA_PICK(C, Q, DD, 16) PA_PICK(C, Q, DD, 32)
+  PA_PICK_B(DT_F16, DT_F16, 64) PA_PICK_B(DT_F16, DT_F16, 128) PA_PICK_B(DT_BF16, DT_BF16, 64)
+  PA_PICK_B(DT_BF16, DT_BF16, 128) PA_PICK_B(DT_FP8, DT_F16, 64) PA_PICK_B(DT_FP8, DT_F16, 128)
+  PA_PICK_B(DT_FP8, DT_BF16, 64) PA_PICK_B(DT_FP8, DT_BF16, 128)
+#undef PA_PICK_B
 #undef PA_PICK
   if (k == nullptr) return 0;
   size_t shm = 0;

@@ -348,7 +348,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   const int G = num_heads / num_kv_heads;
-  const bool mfma_ok = cache_dtype != PA_F32 && block_size == 16 && G <= 16;
+  const bool mfma_ok = cache_dtype != PA_F32 && (block_size == 16 || block_size == 32) && G <= 16;
   bool use_mfma;
   if (variant == PA_VARIANT_MFMA) {
     if (!mfma_ok) return PA_ERR_UNSUPPORTED;
@@ -367,7 +367,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       partition_tokens == 0 && use_mfma && balanced_eligible(num_seqs, num_kv_heads, max_blocks_per_seq);
   int nw = 0;
   if (balanced) {
-    const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, G, num_seqs, stream_kv);
+    const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs,
+                                              stream_kv);
     const int cus = cu_count();
     nw = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
     nw = nw > pa::kMaxBalancedGroups ? pa::kMaxBalancedGroups : nw;
@@ -415,7 +416,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;
   bool timed = begin_event(st, &ev);
-  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, cache_dtype, q_dtype, head_dim, st)
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, cache_dtype, q_dtype, head_dim, block_size, st)
                           : pa::launch_decode_valu(a, cache_dtype, q_dtype, head_dim, block_size, st);
   end_event(timed, st, ev, PA_KERNEL_DECODE_PARTITION);
   if (e != hipSuccess) return PA_ERR_HIP;

@@ -177,7 +177,8 @@ COMBOS = [
     ("bf16", "bf16", 8, 2, 128, 16, 2), ("bf16", "bf16", 16, 2, 64, 16, 2), ("f16", "f16", 8, 1, 128, 16, 2),
     ("bf16", "bf16", 32, 2, 128, 16, 2), ("bf16", "bf16", 4, 4, 128, 16, 2), ("f16", "f16", 6, 3, 128, 16, 0),
     ("fp8", "bf16", 8, 2, 128, 16, 2), ("fp8", "f16", 8, 2, 64, 16, 2), ("fp8", "bf16", 4, 4, 128, 16, 1),
-    ("fp8", "f16", 4, 2, 128, 32, 1),
+    ("fp8", "f16", 4, 2, 128, 32, 1), ("bf16", "bf16", 8, 2, 128, 32, 2), ("f16", "f16", 4, 4, 64, 32, 2),
+    ("fp8", "bf16", 8, 1, 128, 32, 2), ("fp8", "f16", 4, 4, 64, 32, 2),
 ]
 
 
@@ -197,17 +198,17 @@ def test_small_parity(cdt, qdt, hq, hkv, D, B, variant, part):
 
 @pytest.mark.parametrize("lens", [[8192 + 5], [1, 0, 5000, 17, 3000, 16, 0, 2049], [40] * 1100],
                          ids=["one-long", "mixed-with-empty", "many-units"])
-@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
-def test_balanced_split_cuts_units(lens, cdt):
+@pytest.mark.parametrize("cdt,B", [("bf16", 16), ("fp8", 16), ("bf16", 32), ("fp8", 32)])
+def test_balanced_split_cuts_units(lens, cdt, B):
     """On batches of few (sequence, kv head) units the MFMA kernel's default plan spreads the K/V
     evenly over one resident grid: a lone long unit is cut across many work-groups, and empty
     sequences sit between cut units; a batch of many units takes fixed partitions instead.
     Explicit partitions give the same result within tolerance."""
     w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype="bf16",
-                      seed=len(lens) + 7)
+                      block_size=B, seed=len(lens) + 7)
     ref = run_oracle(w)
     got = run_gpu(w, out_dt="f32", variant=2)
-    assert_close(got, ref, cdt, "f32", f"balanced {cdt} S={len(lens)}")
+    assert_close(got, ref, cdt, "f32", f"balanced {cdt} B={B} S={len(lens)}")
     fixed = run_gpu(w, out_dt="f32", part=512, variant=2)
     assert np.max(np.abs(got - fixed)) <= TOL[cdt]
     assert np.array_equal(got, run_gpu(w, out_dt="f32", variant=2))
