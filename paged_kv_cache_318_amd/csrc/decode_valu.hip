@@ -248,6 +248,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // The weights are computed once per part into LDS; every thread then sums over parts in the same
 // order (deterministic), with the partial-output loads unrolled.
 constexpr int kMergeChunk = 1024;
+constexpr int kMergeFast = 8;  // units of at most this many parts take the register path
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block_size) {
@@ -287,6 +288,35 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
     if (!a.balanced) return first_slot + k;
     return k == 0 ? static_cast<size_t>(2 * i0 + (i0_first ? 0 : 1)) : static_cast<size_t>(2 * (i0 + k));
   };
+  if (count <= kMergeFast) {
+    // few parts (the usual case): every (max, sum) and output load of the unit is issued at once,
+    // then the same sums as below in the same order (bit-identical to the general path)
+    float2 ml[kMergeFast];
+    float o[kMergeFast];
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) {
+      if (k < count) {
+        const size_t sl = slot_of(k) * gu + hn;
+        ml[k] = a.ws_ml[sl];
+        o[k] = a.ws_o[sl * D + d];
+      }
+    }
+    float M = neg_inf();
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k)
+      if (k < count) M = fmaxf(M, ml[k].x);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) {
+      if (k < count) {
+        const float wk = ml[k].y * __builtin_amdgcn_exp2f(ml[k].x - M);
+        den += wk;
+        num = __builtin_fmaf(wk, o[k], num);
+      }
+    }
+    store_out(a.out, orow + d, num / den, a.out_dtype);
+    return;
+  }
   float M = neg_inf();
   for (int k = d; k < count; k += D) M = fmaxf(M, a.ws_ml[slot_of(k) * gu + hn].x);
 #pragma unroll
