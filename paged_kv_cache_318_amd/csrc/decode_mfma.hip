@@ -270,8 +270,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     float tm = z[0];
 #pragma unroll
     for (int i = 1; i < 4 * NBI; ++i) tm = fmaxf(tm, z[i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = pair32_max(pair16_max(tm));
     const float mn = fmaxf(m, tm);  // finite: every block of the sequence holds a valid token
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float pz[4 * NBI];
@@ -333,8 +332,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
 
   // per-column sum over the four lane groups, then merge the four waves through LDS
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = pair32_sum(pair16_sum(lsum));
   float* sm_m = smem;
   float* sm_l = smem + 64;
   float* sm_o = smem + 128;  // [4 waves][G][D]

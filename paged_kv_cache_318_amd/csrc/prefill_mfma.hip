@@ -7,16 +7,18 @@
 // L tokens (the chunk's keys and values already written) has queries at positions L-n .. L-1.
 //
 // Rows: the n * G (query token, query head of the kv group) pairs of one (sequence, kv head),
-// token-major. One work-group (4 wave64s) takes 64 consecutive rows, each wave 16 of them as the
-// 16 columns of the same 16x16x32 MFMA the decode kernel uses:
+// token-major. One work-group (4 wave64s) takes 128 consecutive rows (64 for fp8 at D = 128);
+// each wave takes two sets of 16 (one), each set the 16 columns of the same 16x16x32 MFMA the
+// decode kernel uses:
 //     Z^T[16 tokens][16 rows]  = K_tile[16][D] . Q^T[D][16 rows]        (scores)
 //     O^T[D][16 rows]         += V^T[D][32 tokens] . P^T[32 tokens][16 rows]
-// so every K/V tile is fetched once per 64 rows. Per iteration the work-group stages two blocks'
-// key and value tiles (16 KB at 16 bits) in LDS with gfx950's direct global -> LDS loads (1 KB
-// contiguous per load instruction; keys XOR-swizzled by row so the MFMA-layout reads hit distinct
-// banks), then every wave runs its scores, its online softmax and its weighted values out of LDS.
-// Each column carries its own causal limit (its query position); a wave's rows never leave it,
-// so no cross-wave merge is needed and no workspace either.
+// so every K/V tile is fetched once per 128 rows, and every key or value operand read from LDS
+// feeds both sets. Per iteration the work-group stages two blocks' key and value tiles (16 KB at
+// 16 bits) in LDS with gfx950's direct global -> LDS loads (1 KB contiguous per load
+// instruction; keys XOR-swizzled by row so the MFMA-layout reads hit distinct banks), then every
+// wave runs its scores, its online softmax and its weighted values out of LDS. Each column
+// carries its own causal limit (its query position); a wave's rows never leave it, so no
+// cross-wave merge is needed and no workspace either.
 
 #include <type_traits>
 
@@ -26,20 +28,38 @@
 
 namespace pa {
 
-constexpr int kPrefillRows = 64;  // rows per work-group (4 waves x 16 MFMA columns)
+// Column sets per wave: each wave takes CW sets of 16 rows, so every key or value operand read
+// from LDS feeds CW MFMAs (one per set). Two sets halve the LDS reads, the K/V fetches and the
+// barriers per row; the fp8 instances at D = 128 keep one (their converted operands would spill).
+template <int CDT, int D>
+constexpr int prefill_column_sets() { return (CDT == DT_FP8 && D == 128) ? 1 : 2; }
+template <int CDT, int D>
+constexpr int prefill_rows() { return 64 * prefill_column_sets<CDT, D>(); }  // rows per work-group
+
+// Iterations in flight: a ring of this many LDS buffers, so the loads of the next NS-1
+// iterations fly while one computes. 2, 3 and 4 stages measured the same (the loop is bound by
+// its own issue and latency, not by the loads), so the ring stays at the smallest.
+constexpr int kPrefillStages = 2;
+
+// Bytes of one stage: the key tiles of two blocks, their value tiles and, for fp8 caches, 256
+// bytes whose first 16 hold the two blocks' key and value scales.
+template <int CDT, int D>
+constexpr size_t prefill_stage_bytes() {
+  return size_t{4} * 16 * D * Elem<CDT>::bytes + (CDT == DT_FP8 ? 256 : 0);
+}
 
 template <int CDT, int D>
 constexpr size_t prefill_lds_bytes() {
-  // two buffers, each the key tiles of two blocks followed by their value tiles
-  return size_t{2} * 4 * 16 * D * Elem<CDT>::bytes;
+  return size_t{kPrefillStages} * prefill_stage_bytes<CDT, D>();
 }
 
-// 3 wave64s per SIMD (at most 168 registers a lane); the fp8 instances at D = 128 need a few
-// more for their converted operands and run at 2 rather than spill.
+// Two column sets: 2 wave64s per SIMD (at most 256 registers a lane). One set (fp8, D = 128):
+// also 2, for the registers of its converted operands.
 template <int CDT, int QDT, int D>
-__global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void prefill_mfma_kernel(
-    PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int B = 16;
+  constexpr int CW = prefill_column_sets<CDT, D>();
+  constexpr int ROWS = prefill_rows<CDT, D>();
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int KK = D / 32;                 // score MFMAs per block
   constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
@@ -49,8 +69,17 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
   constexpr int RPI = 64 / CPR;              // key rows per 1 KB load
   constexpr int NCH = KT / 1024;             // 1 KB loads per tile
   static_assert(NCH >= 1 && KT % 1024 == 0, "tile must be a whole number of 1 KB loads");
+  constexpr int NS = kPrefillStages;
+  constexpr int SB = static_cast<int>(prefill_stage_bytes<CDT, D>());
+  // vector-memory operations one issue() makes per wave: its 1 KB loads, plus (fp8) the load of
+  // the two blocks' scales
+  constexpr int OPS = NCH + (CDT == DT_FP8 ? 1 : 0);
+  static_assert((NS - 2) * OPS <= 63, "vmcnt field");
+  // vmcnt((NS-2)*OPS) lgkmcnt(0): every load but those of the NS-2 iterations issued after
+  // this one, and every LDS access
+  constexpr int kWaitOldest = (((NS - 2) * OPS) & 15) | (7 << 4) | ((((NS - 2) * OPS) >> 4) << 14);
   extern __shared__ float smem[];
-  // [2 buffers][keys of blocks A, B][values of blocks A, B (dim-major, as stored)], KT bytes each
+  // [NS stages][keys of blocks A, B][values of blocks A, B (dim-major, as stored)][fp8 scales]
   uint8_t* kt = reinterpret_cast<uint8_t*>(smem);
 
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -66,34 +95,28 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
   q1 = q1 < q0 ? q0 : (q1 > a.num_tokens ? a.num_tokens : q1);
   const int ns = (q1 - q0) < L ? (q1 - q0) : L;  // a chunk cannot be longer than the sequence
   const int rows = ns * G;
-  const int r0 = tile * kPrefillRows;
+  const int r0 = tile * ROWS;
   if (r0 >= rows) return;
-  const int rlast = (r0 + kPrefillRows < rows ? r0 + kPrefillRows : rows) - 1;
+  const int rlast = (r0 + ROWS < rows ? r0 + ROWS : rows) - 1;
   const int nblk = (L - ns + rlast / G) / B + 1;   // blocks up to the group's last query
 
-  // this lane's column: row r = (token k of the chunk, head hh of the group); rows past the
-  // chunk attend token 0 only (finite, discarded)
-  const int r = r0 + wave * 16 + n;
-  const bool live = r < rows;
-  const int k = live ? r / G : 0;
-  const int hh = live ? r - k * G : 0;
-  const int pos = live ? L - ns + k : 0;
+  // this lane's columns: row r = (token k of the chunk, head hh of the group) of set c; rows past
+  // the chunk attend token 0 only (finite, discarded)
+  const int wrow = r0 + wave * 16 * CW;
+  bool live[CW];
+  int kq[CW], hh[CW], pos[CW];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const int r = wrow + 16 * c + n;
+    live[c] = r < rows;
+    kq[c] = live[c] ? r / G : 0;
+    hh[c] = live[c] ? r - kq[c] * G : 0;
+    pos[c] = live[c] ? L - ns + kq[c] : 0;
+  }
   // earliest query position among the wave's columns (0 if the wave has rows past the chunk,
   // which attend token 0 only)
-  const int wrow = r0 + wave * 16;
-  const int wave_min_pos = wrow + 15 < rows ? L - ns + wrow / G : 0;
+  const int wave_min_pos = wrow + 16 * CW - 1 < rows ? L - ns + wrow / G : 0;
 
-  u32x4 qop[KK];
-  if (live) {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const uint8_t*>(a.q) +
-        ((static_cast<size_t>(q0 + k) * Hq + g * G + hh) * D) * 2);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qop[kk] = qp[dim_base<EB>(q4, kk) / 8];
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qop[kk] = u32x4{0u, 0u, 0u, 0u};
-  }
 
   // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: tile c / NCH (0, 1: keys of
   // blocks A, B; 2, 3: their values), part c % NCH of it.
@@ -135,18 +158,23 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
 #pragma unroll
   for (int i = 0; i < KL; ++i) kread[i] = n * CPR * 16 + 16 * ((4 * i + q4) ^ (n % CPR));
 
-  f32x4 acc[MI];
+  f32x4 acc[CW][MI];
+  float m[CW], lsum[CW];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = neg_inf(), lsum = 0.0f;
+  for (int c = 0; c < CW; ++c) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) acc[c][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = neg_inf();
+    lsum[c] = 0.0f;
+  }
 
   // Iteration i covers blocks 2i and 2i+1 (the second may lie past the group's last query).
-  // Its tiles go to LDS buffer i & 1: the loads for i+1 are issued right after the barrier that
-  // opens iteration i, so they fly while iteration i computes.
+  // Its tiles go to LDS buffer i % NS: the loads for i+NS-1 are issued right after the barrier
+  // that opens iteration i (every wave is then done with buffer (i-1) % NS), so NS-1 iterations
+  // of loads fly while iteration i computes.
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
   const int niter = (nblk + 1) / 2;
   int tv = 0, tbase = -64;
-  float zs_next[2], vs_next[2];
   auto issue = [&](int it) {
     const int j0 = 2 * it;
     if (j0 - tbase >= 64) {  // next 64 table entries into one VGPR, read back with readlane
@@ -161,53 +189,92 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
     const int pbb = j0 + 1 < nblk ? __builtin_amdgcn_readlane(tv, j0 + 1 - tbase) : pba;
     const size_t offa = (static_cast<size_t>(pba) * Hkv + g) * KT;
     const size_t offb = (static_cast<size_t>(pbb) * Hkv + g) * KT;
-    uint8_t* buf = kt + (it & 1) * (4 * KT);
+    uint8_t* buf = kt + (it % NS) * SB;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const uint8_t* src = (ld_key[i] ? a.k_cache : a.v_cache) + (ld_b[i] ? offb : offa) + ld_src[i];
       dma16<0>(src, buf + ld_dst[i]);
     }
-    zs_next[0] = zs_next[1] = a.zscale;
-    vs_next[0] = vs_next[1] = 1.0f;
     if constexpr (CDT == DT_FP8) {
-      zs_next[0] *= a.k_scale[static_cast<size_t>(pba) * Hkv + g];
-      zs_next[1] *= a.k_scale[static_cast<size_t>(pbb) * Hkv + g];
-      vs_next[0] = a.v_scale[static_cast<size_t>(pba) * Hkv + g];
-      vs_next[1] = a.v_scale[static_cast<size_t>(pbb) * Hkv + g];
+      // 4 bytes a lane into the stage's scale slot: lane l holds (k A, k B, v A, v B)[l % 4]
+      // (every wave writes the same values; each issues it, so all count the same loads)
+      const float* sp = (lane & 2) ? a.v_scale : a.k_scale;
+      __builtin_amdgcn_global_load_lds(
+          (gbl_void_t*)(sp + static_cast<size_t>((lane & 1) ? pbb : pba) * Hkv + g),
+          (lds_void_t*)(buf + 4 * KT), 4, 0, 0);
     }
   };
-  issue(0);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < niter) issue(j);
+  // the query operands, loaded behind the first tiles; then one full wait, so that the loop
+  // starts with nothing in flight but what its own waits account for
+  u32x4 qop[CW][KK];
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    if (live[c]) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const uint8_t*>(a.q) +
+          ((static_cast<size_t>(q0 + kq[c]) * Hq + g * G + hh[c]) * D) * 2);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qop[c][kk] = qp[dim_base<EB>(q4, kk) / 8];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qop[c][kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   for (int it = 0; it < niter; ++it) {
     const int j0 = 2 * it;
     const bool has_b = j0 + 1 < nblk;
-    const float zs[2] = {zs_next[0], zs_next[1]};
-    const float vs[2] = {vs_next[0], vs_next[1]};
-    // This wave's loads for iteration it have landed (both counters drained: nothing newer is in
-    // flight); after the barrier every wave's have, and every wave is done reading the buffer the
-    // next loads go to.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < niter) issue(it + 1);
-    const uint8_t* kb0 = kt + (it & 1) * (4 * KT);
+    const int slot = it % NS;
+    // This wave's loads for iteration it have landed: the vector-memory counter is down to the
+    // loads of the iterations issued after it (all of them near the end, when fewer are left)
+    // and the LDS counter has drained. After the barrier every wave's have, and every wave is
+    // done reading buffer (it-1) % NS, which the loads issued below go to.
+    // The barrier is a bare s_barrier behind these explicit waits (the compiler's own barrier
+    // lowering waits for every load in flight, which would drain the ring each iteration); the
+    // empty asm statements keep the compiler from moving memory accesses across it.
+    if (it + NS - 2 < niter) __builtin_amdgcn_s_waitcnt(kWaitOldest);
+    else __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* kb0 = kt + slot * SB;
     const uint8_t* vt = kb0 + 2 * KT;
+    float zs[2] = {a.zscale, a.zscale}, vs[2] = {1.0f, 1.0f};
+    if constexpr (CDT == DT_FP8) {
+      const float* scl = reinterpret_cast<const float*>(kb0 + 4 * KT);
+      zs[0] *= scl[0];
+      zs[1] *= scl[1];
+      vs[0] = scl[2];
+      vs[1] = scl[3];
+    }
+    if (it + NS - 1 < niter) issue(it + NS - 1);
 
-    f32x4 zt[2];
+    // scores: each key operand read once from LDS, multiplied into every column set
+    f32x4 zt[CW][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CW; ++c) zt[c][u] = f32x4{0.f, 0.f, 0.f, 0.f};
       const uint8_t* kb = kb0 + u * KT;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
         if constexpr (EB == 2) {
-          zt[u] = mfma_k32<QDT>(raw, qop[i], zt[u]);
+#pragma unroll
+          for (int c = 0; c < CW; ++c) zt[c][u] = mfma_k32<QDT>(raw, qop[c][i], zt[c][u]);
         } else {
           const u32x4 k0{fp8x2_to16<QDT, false>(raw.x), fp8x2_to16<QDT, true>(raw.x),
                          fp8x2_to16<QDT, false>(raw.y), fp8x2_to16<QDT, true>(raw.y)};
-          zt[u] = mfma_k32<QDT>(k0, qop[2 * i], zt[u]);
           const u32x4 k1{fp8x2_to16<QDT, false>(raw.z), fp8x2_to16<QDT, true>(raw.z),
                          fp8x2_to16<QDT, false>(raw.w), fp8x2_to16<QDT, true>(raw.w)};
-          zt[u] = mfma_k32<QDT>(k1, qop[2 * i + 1], zt[u]);
+#pragma unroll
+          for (int c = 0; c < CW; ++c) {
+            zt[c][u] = mfma_k32<QDT>(k0, qop[c][2 * i], zt[c][u]);
+            zt[c][u] = mfma_k32<QDT>(k1, qop[c][2 * i + 1], zt[c][u]);
+          }
         }
       }
     }
@@ -216,51 +283,55 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
     const bool interior = (j0 + 2) * B - 1 <= wave_min_pos;
     auto step = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      // lane (q4, n) holds tokens t0(u) .. t0(u)+3 of block j0+u for column n
-      float z[8];
+      // per column set: online softmax of lane (q4, n)'s tokens t0(u) .. t0(u)+3 of block j0+u
+      u32x4 phi[CW], plo[CW];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t0 = (j0 + u) * B + 4 * q4;
+      for (int c = 0; c < CW; ++c) {
+        float z[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int t0 = (j0 + u) * B + 4 * q4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (MASKED)
+              z[4 * u + i] = (t0 + i <= pos[c] && (u == 0 || has_b)) ? zt[c][u][i] * zs[u] : neg_inf();
+            else
+              z[4 * u + i] = zt[c][u][i] * zs[u];
+          }
+        }
+        float tm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+        tm = pair32_max(pair16_max(tm));
+        // The running max only moves when some column of the set sees a larger score; the
+        // accumulators are rescaled only then (the result is the same for any common shift).
+        if (__builtin_amdgcn_ballot_w64(tm > m[c]) != 0) {
+          const float mn = fmaxf(m[c], tm);  // finite: block 0 holds token 0, which every column attends
+          const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
+          lsum[c] *= alpha;
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) acc[c][mi] = acc[c][mi] * alpha;
+          m[c] = mn;
+        }
+        float pz[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pz[i] = __builtin_amdgcn_exp2f(z[i] - m[c]);
+          lsum[c] += pz[i];
+        }
+        // P^T as 16-bit hi part + remainder
+        uint32_t phw[4], plw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if constexpr (MASKED)
-            z[4 * u + i] = (t0 + i <= pos && (u == 0 || has_b)) ? zt[u][i] * zs[u] : neg_inf();
-          else
-            z[4 * u + i] = zt[u][i] * zs[u];
+          const float vsc = i < 2 ? vs[0] : vs[1];
+          const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
+          phw[i] = pack16x2<QDT>(p0, p1);
+          plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
         }
+        phi[c] = u32x4{phw[0], phw[1], phw[2], phw[3]};
+        plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
       }
-      float tm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      // The running max only moves when some column of the wave sees a larger score; the
-      // accumulators are rescaled only then (the result is the same for any common shift).
-      if (__builtin_amdgcn_ballot_w64(tm > m) != 0) {
-        const float mn = fmaxf(m, tm);  // finite: block 0 holds token 0, which every column attends
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
-        m = mn;
-      }
-      float pz[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pz[i] = __builtin_amdgcn_exp2f(z[i] - m);
-        lsum += pz[i];
-      }
-      // weighted values over the 32 tokens of the two blocks; P^T as 16-bit hi part +
-      // remainder; slots at or beyond L (never written) get zero values
-      uint32_t phw[4], plw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vsc = i < 2 ? vs[0] : vs[1];
-        const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
-        phw[i] = pack16x2<QDT>(p0, p1);
-        plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
-      }
-      const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
-      const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};
+      // weighted values over the 32 tokens of the two blocks; slots at or beyond L (never
+      // written) get zero values
       uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
       if constexpr (MASKED) {
         const int va = L - j0 * B - 4 * q4;                   // this lane group's tokens below L
@@ -293,32 +364,40 @@ __global__ __launch_bounds__(256, (CDT == DT_FP8 && D == 128) ? 2 : 3) void pref
         if constexpr (MASKED) return u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
         else return u32x4{a0, a1, c0, c1};
       };
-      // groups of 4 value tiles: the hi MFMAs of the group, then its remainder MFMAs, so no MFMA
-      // waits on the one just issued into the same accumulator
+      // each value operand read once from LDS and multiplied into every column set; groups of
+      // 4 value tiles (hi MFMAs of the group, then its remainder MFMAs) so no MFMA waits on the
+      // one just issued into the same accumulator
+      constexpr int GV = CW == 1 ? 4 : 2;
 #pragma unroll
-      for (int m0 = 0; m0 < MI; m0 += 4) {
-        u32x4 vop[4];
+      for (int m0 = 0; m0 < MI; m0 += GV) {
+        u32x4 vop[GV];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < GV; ++j) {
           vop[j] = vop_of(m0 + j);
-          acc[m0 + j] = mfma_k32<QDT>(vop[j], phi, acc[m0 + j]);
+#pragma unroll
+          for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], phi[c], acc[c][m0 + j]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m0 + j] = mfma_k32<QDT>(vop[j], plo, acc[m0 + j]);
+        for (int j = 0; j < GV; ++j)
+#pragma unroll
+          for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], plo[c], acc[c][m0 + j]);
       }
     };
     if (interior) step(std::false_type{});
     else step(std::true_type{});
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (live) {
-    const size_t orow = (static_cast<size_t>(q0 + k) * Hq + g * G + hh) * D;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const f32x4 o{acc[mi][0] / lsum, acc[mi][1] / lsum, acc[mi][2] / lsum, acc[mi][3] / lsum};
-      store_out4(a.out, orow + 16 * mi + 4 * q4, o, a.out_dtype);
+  for (int c = 0; c < CW; ++c) {
+    float ls = lsum[c];
+    ls = pair32_sum(pair16_sum(ls));
+    if (live[c]) {
+      const size_t orow = (static_cast<size_t>(q0 + kq[c]) * Hq + g * G + hh[c]) * D;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const f32x4 o{acc[c][mi][0] / ls, acc[c][mi][1] / ls, acc[c][mi][2] / ls, acc[c][mi][3] / ls};
+        store_out4(a.out, orow + 16 * mi + 4 * q4, o, a.out_dtype);
+      }
     }
   }
 }
@@ -327,8 +406,8 @@ template <int CDT, int QDT, int D>
 static hipError_t launch_prefill_dn(const PrefillArgs& a, int max_query_len, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
   const long long rows = static_cast<long long>(max_query_len) * G;
-  const dim3 grid(static_cast<unsigned>((rows + kPrefillRows - 1) / kPrefillRows), a.num_kv_heads,
-                  a.num_seqs);
+  constexpr int R = prefill_rows<CDT, D>();
+  const dim3 grid(static_cast<unsigned>((rows + R - 1) / R), a.num_kv_heads, a.num_seqs);
   const size_t shm = prefill_lds_bytes<CDT, D>();
   hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
