@@ -329,7 +329,9 @@ def kernel_source_hash(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_318_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("pa_device.h", "decode_valu.hip" if kernel == "decode_valu" else "decode_mfma.hip"):
+    files = ["pa_device.h", "pa_sched.h", "kv_write.h"]
+    files += ["decode_valu.hip"] if kernel == "decode_valu" else ["mfma_common.h", "decode_mfma.hip"]
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
