@@ -216,7 +216,7 @@ def measure_paging(args, lib, torch):
     """The pages say the paged kernel pays for its indirection and that the block size trades
     table overhead against the unused tail. Same kernel, same lengths: blocks scattered through the
     pool vs handed out in address order (every sequence contiguous), for block sizes 8, 16 and 32,
-    on the MHA batch (VALU kernel) and the GQA batch (MFMA kernel at 16 and 32, VALU at 8)."""
+    on the MHA batch (VALU kernel) and the GQA batch (MFMA kernel)."""
     from paged_kv_cache_318_amd.step import workspace_for
     from workloads.synth import config_lens
     rows = []
@@ -250,7 +250,7 @@ def measure_paging(args, lib, torch):
                 G = spec["num_heads"] // spec["num_kv_heads"]
                 rows.append({
                     "workload": spec["name"], "block_size": B, "placement": placement,
-                    "kernel": "decode_mfma" if (B in (16, 32) and G >= 2) else "decode_valu",
+                    "kernel": "decode_mfma" if G >= 2 else "decode_valu",
                     "attention_us": round(us, 2),
                     "merge_us": round(1e3 * m_ms / m_n, 2) if m_n else None,
                     "kv_gbs": round(kv / (us * 1e-6) / 1e9, 1),
@@ -443,13 +443,26 @@ def main():
     w_ms, w_n = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
     c_ms, c_n = lib.pa_profile_read(lib.PA_KERNEL_COPY_BLOCKS)
     lib.pa_profile_enable(False)
+    # a third pass with an event before every step and after the last: the spread of step times
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for i in range(args.steps):
+        evs[i].record()
+        step(args.warmup + 2 * args.steps + i)
+    evs[-1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+
+    def pct(q):
+        return round(per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))], 2)
+
+    step_pcts = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
     k_avg_ms = k_ms / max(k_n, 1)
     G = w.num_heads // w.num_kv_heads
-    mfma_ok = w.dtype != "f32" and w.block_size == 16 and G <= 16
+    mfma_ok = w.dtype != "f32" and G <= 16
     kernel = "decode_mfma" if (args.variant == 2 or (args.variant == 0 and mfma_ok and G >= 2)) \
         else "decode_valu"
     unique = args.config == 4
@@ -489,6 +502,7 @@ def main():
             "write_kv": round(1e3 * w_ms / max(w_n, 1), 2) if w_n else None,
             "copy_blocks": round(1e3 * c_ms / max(c_n, 1), 2) if c_n else None,
         },
+        "step_us_percentiles": step_pcts,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -155,8 +155,8 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
  *   out_dtype: q_dtype or PA_F32. Accumulation is fp32 throughout.
  *   k_scale / v_scale: required for fp8 caches (one scale per block and kv head).
  *   num_heads % num_kv_heads == 0; head_dim in {64, 128}; block_size in {8, 16, 32}.
- *   variant: pa_variant; PA_VARIANT_MFMA needs a 16-bit or fp8 cache, block_size 16 or 32 and at
- *   most 16 query heads per kv head.
+ *   variant: pa_variant; PA_VARIANT_MFMA needs a 16-bit or fp8 cache and at most 16 query heads
+ *   per kv head (any supported block size).
  *   flags: 0 or PA_DECODE_SHARED_BLOCKS (a hint, never a change of result): several sequences of
  *   the batch reference the same physical blocks (shared prefixes, parallel samples), so K/V are
  *   read through the caches and a shared block fetched for one sequence is reused by the others.

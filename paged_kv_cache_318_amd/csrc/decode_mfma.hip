@@ -64,32 +64,48 @@ template <int CDT, int QDT, int D, int B, bool NT>
 __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, int s, int g, int L,
                                              int b0, int b1, bool final_out, size_t slot) {
   constexpr int EB = Elem<CDT>::bytes;
-  constexpr int SUB = B / 16;                // 16-token tiles per block
+  // Work items: one block (B >= 16: SUB = B/16 tiles of 16 tokens) or, for B = 8, a pair of
+  // consecutive blocks forming one 16-token tile (key rows and value token columns 0-7 from the
+  // first block, 8-15 from the second).
+  static_assert(B == 8 || B == 16 || B == 32, "block size");
+  constexpr bool PAIR = B < 16;
+  constexpr int GB = PAIR ? 16 / B : 1;      // blocks per work item
+  constexpr int SUB = PAIR ? 1 : B / 16;     // 16-token tiles per work item
   constexpr int KK = D / 32;                 // score MFMAs per tile
   constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
-  constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per block
+  constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per tile
   constexpr int KT = 16 * D * EB;            // bytes of one 16-token key tile
   constexpr int KTB = B * D * EB;            // bytes of one (block, kv head) key or value tile
   constexpr int CPR = D * EB / 16;           // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;              // key rows per 1 KB load instruction
   constexpr int NI = 16 / RPI;               // load instructions per key tile
   constexpr int NBI = mfma_blocks_per_iter(EB);  // 16-token tiles per iteration (16 KB in flight)
-  constexpr int BPI = NBI / SUB;             // blocks per iteration
-  static_assert(BPI >= 1 && NBI % SUB == 0, "an iteration takes whole blocks");
+  constexpr int BPI = NBI / SUB;             // work items per iteration
+  constexpr int CHUNK = 64 / GB;             // work items whose table entries one VGPR holds
+  static_assert(BPI >= 1 && NBI % SUB == 0, "an iteration takes whole work items");
   constexpr int kKeyAux = NT ? 2 : 0;        // cache policy of the key loads (2: non-temporal)
   constexpr bool kNtV = NT;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, n = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int nitems = (b1 - b0 + GB - 1) / GB;
+  // tokens at or beyond lim belong to a later segment or to no one (the second block of a pair
+  // may lie past the segment's end)
+  const int lim = min(L, b1 * B);
+  // first token of tile u of work item k (relative to the segment)
+  auto tile_start = [&](int k, int u) { return (b0 + GB * k) * B + 16 * (u % SUB); };
+  // PAIR: the block (0: first, 1: second) holding this lane's tokens 4*q4 .. 4*q4+3 of a tile
+  const bool lane_second = PAIR && q4 >= 2;
   // pa_decode_append: the segment holding the unit's last block substitutes the new token
-  // (position L-1, offset o_new of that block) for what the cache holds there -- in the staged
-  // key tile and in the value registers -- and stores the key row and the whole value tile back
-  // (whole lines rather than one element per dim row).
+  // (position L-1, row o_new of its tile) for what the cache holds there -- in the staged key
+  // tile and in the value registers -- and stores the key row and the value tile rows of its
+  // block back (whole lines rather than one element per dim row).
   const int nblk_all = (L + B - 1) / B;
   const int slot_new = (a.new_slots != nullptr && b1 == nblk_all) ? new_token_slot(a, s, L, B) : -1;
-  const int o_new = (L - 1) % 16;            // within its 16-token tile
-  const int sub_new = ((L - 1) % B) / 16;     // which tile of its block
+  const int item_new = (nblk_all - 1 - b0) / GB;  // (meaningful only when slot_new >= 0)
+  const int sub_new = PAIR ? 0 : ((L - 1) % B) / 16;
+  const int o_new = (L - 1) - tile_start(item_new, sub_new);
 
   u32x4 qop[KK];
   if (n < G) {
@@ -106,67 +122,84 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // Key tiles are staged through this wave's NBI LDS slots. Load instruction ii of a tile covers
   // 1 KB of it contiguously (rows RPI*ii .. RPI*ii+RPI-1); lane l fetches 16-byte chunk
   // (l % CPR) ^ (row % CPR) of its row, so LDS holds each row XOR-swizzled by its index and the
-  // score-operand reads below (16 rows at one chunk column) fall into distinct banks.
+  // score-operand reads below (16 rows at one chunk column) fall into distinct banks. PAIR: rows
+  // 0-7 come from the first block, 8-15 from the second (dsec: this lane's row is in the second).
   uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT);
   int dsrc[NI];
+  bool dsec[NI];
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int row = RPI * ii + lane / CPR;
-    dsrc[ii] = row * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
+    dsec[ii] = PAIR && row >= B;
+    dsrc[ii] = (dsec[ii] ? row - B : row) * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
   }
   int kread[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) kread[i] = n * CPR * 16 + 16 * ((4 * i + q4) ^ (n % CPR));
+  // this lane's value-operand offset inside a block's [D][B] value tile (dim row n, tokens
+  // 4*q4 .. 4*q4+3 of the tile), before the tile's token column and the row group mi
+  const int vlane = (n * B + 4 * (PAIR ? q4 % 2 : q4)) * EB;
 
   f32x4 acc[MI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), lsum = 0.0f;
 
-
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  // this wave's blocks are b0 + wave + 4*i, taken BPI per iteration (NBI 16-token tiles: tile u
-  // is 16-token part u % SUB of block u / SUB); their table entries are fetched 64 at a time into
-  // one VGPR and read back with readlane
-  const int nmine = b0 + wave < b1 ? (b1 - b0 - wave + 3) / 4 : 0;
-  for (int base_i = 0; base_i < nmine; base_i += 64) {
-  const int cnt = min(64, nmine - base_i);
+  // this wave's work items are wave + 4*i, taken BPI per iteration (NBI 16-token tiles: tile u is
+  // 16-token part u % SUB of item u / SUB); their table entries are fetched CHUNK items at a time
+  // into one VGPR (lane GB*j + h: block h of item j) and read back with readlane
+  const int nmine = wave < nitems ? (nitems - wave + 3) / 4 : 0;
+  for (int base_i = 0; base_i < nmine; base_i += CHUNK) {
+  const int cnt = min(CHUNK, nmine - base_i);
   int tv = 0;
-  if (lane < cnt) {
-    tv = trow[b0 + wave + 4 * (base_i + lane)];
+  if (lane < cnt * GB) {
+    // a pair's second block past the segment's end stands in as its first block: its tokens are
+    // masked, but its scales multiply zero weights, so they must be those of a block in use (a
+    // free block's may be anything, NaN included)
+    const int blk = b0 + GB * (wave + 4 * (base_i + lane / GB)) + lane % GB;
+    tv = trow[blk < b1 ? blk : blk - 1];
     tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
   }
   for (int it = 0; it < cnt; it += BPI) {
-    const int nlive = min(BPI, cnt - it);  // blocks of this iteration (the last may have fewer)
-    const int ja = b0 + wave + 4 * (base_i + it);
-    int pbs[NBI];
-    size_t offs[NBI], voffs[NBI];  // key tile start; value tile start + the tile's token column
+    const int nlive = min(BPI, cnt - it);  // work items of this iteration (the last may have fewer)
+    const int ia = wave + 4 * (base_i + it);  // the iteration's first work item
+    // per tile: base of its (first) block's (block, kv head) tiles, of the second block (PAIR)
+    size_t ba[NBI], bb[NBI];
+    int pba[NBI], pbb[NBI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
-      pbs[u] = __builtin_amdgcn_readlane(tv, it + (u / SUB < nlive ? u / SUB : 0));
-      const size_t bt = (static_cast<size_t>(pbs[u]) * Hkv + g) * KTB;
-      offs[u] = bt + (u % SUB) * KT;
-      voffs[u] = bt + (u % SUB) * 16 * EB;
+      const int j = it + (u / SUB < nlive ? u / SUB : 0);
+      pba[u] = __builtin_amdgcn_readlane(tv, GB * j);
+      pbb[u] = PAIR ? __builtin_amdgcn_readlane(tv, GB * j + 1) : pba[u];
+      ba[u] = (static_cast<size_t>(pba[u]) * Hkv + g) * KTB;
+      bb[u] = (static_cast<size_t>(pbb[u]) * Hkv + g) * KTB;
     }
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
-      if (u / SUB >= nlive) break;
+      if (u / SUB < nlive) {
 #pragma unroll
-      for (int ii = 0; ii < NI; ++ii)
-        dma16<kKeyAux>(a.k_cache + offs[u] + dsrc[ii], kbuf + u * KT + 1024 * ii);
+        for (int ii = 0; ii < NI; ++ii)
+          dma16<kKeyAux>(a.k_cache + (dsec[ii] ? bb[u] : ba[u]) + (u % SUB) * KT + dsrc[ii],
+                         kbuf + u * KT + 1024 * ii);
+      }
     }
+    // value tile rows of tile u for this lane: its block, the tile's token column
+    size_t vrow[NBI];
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) vrow[u] = (lane_second ? bb[u] : ba[u]) + (u % SUB) * 16 * EB + vlane;
     Raw<4 * EB> vr[NBI][MI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + voffs[u] + ((16 * mi + n) * B + 4 * q4) * EB);
-    // the new token's rows, fetched along with the tile they go into (block u_new of this
+        vr[u][mi] = load_raw<4 * EB, kNtV>(a.v_cache + vrow[u] + 16 * mi * B * EB);
+    // the new token's rows, fetched along with the tile they go into (tile u_new of this
     // iteration, if any): lane l < D/8 the key dims 8l .. 8l+7, lane (q4, n) value dims 16*mi + n
     int u_new = -1;
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
-      if (slot_new >= 0 && u / SUB < nlive && ja + 4 * (u / SUB) == nblk_all - 1 && u % SUB == sub_new)
+      if (slot_new >= 0 && u / SUB < nlive && ia + 4 * (u / SUB) == item_new && u % SUB == sub_new)
         u_new = u;
     u32x4 knew{0u, 0u, 0u, 0u};
     uint32_t vnew[MI / 2];  // two 16-bit values a register
@@ -180,14 +213,23 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
         vnew[mi / 2] = static_cast<uint32_t>(vn[16 * mi + n]) | (static_cast<uint32_t>(vn[16 * mi + 16 + n]) << 16);
     }
 
-    float zs[NBI], vs[NBI];
+    // key and value scales of the lane's tokens of each tile (fp8; the key scale folded into zscale)
+    float zs_l[NBI], vs_l[NBI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
-      zs[u] = a.zscale;
-      vs[u] = 1.0f;
+      zs_l[u] = a.zscale;
+      vs_l[u] = 1.0f;
       if constexpr (CDT == DT_FP8) {
-        zs[u] *= a.k_scale[static_cast<size_t>(pbs[u]) * Hkv + g];
-        vs[u] = a.v_scale[static_cast<size_t>(pbs[u]) * Hkv + g];
+        const size_t ia_s = static_cast<size_t>(pba[u]) * Hkv + g;
+        float ks = a.k_scale[ia_s], vsc = a.v_scale[ia_s];
+        if constexpr (PAIR) {
+          const size_t ib_s = static_cast<size_t>(pbb[u]) * Hkv + g;
+          const float ks2 = a.k_scale[ib_s], vs2 = a.v_scale[ib_s];
+          ks = lane_second ? ks2 : ks;
+          vsc = lane_second ? vs2 : vsc;
+        }
+        zs_l[u] *= ks;
+        vs_l[u] = vsc;
       }
     }
     // The direct-to-LDS loads have landed only once both the vector-memory counter and the LDS
@@ -196,17 +238,13 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     __builtin_amdgcn_s_waitcnt(0);
 
     if (u_new >= 0) {
-      int pbn = pbs[0];
-      size_t offn = offs[0];  // the new token's key tile
-#pragma unroll
-      for (int u = 1; u < NBI; ++u)
-        if (u == u_new) {
-          pbn = pbs[u];
-          offn = offs[u];
-        }
-      float ks = 1.0f;
-      if constexpr (CDT == DT_FP8) ks = a.k_scale[static_cast<size_t>(pbn) * Hkv + g];
-      uint8_t* kslot = const_cast<uint8_t*>(a.k_cache) + offn + o_new * D * EB;
+      const size_t pbn = static_cast<size_t>(slot_new / B);  // the new token's block
+      float ks = 1.0f, vsn = 1.0f;
+      if constexpr (CDT == DT_FP8) {
+        ks = a.k_scale[pbn * Hkv + g];
+        vsn = a.v_scale[pbn * Hkv + g];
+      }
+      uint8_t* kslot = const_cast<uint8_t*>(a.k_cache) + (pbn * Hkv + g) * KTB + (slot_new % B) * D * EB;
       uint8_t* krow_lds = kbuf + u_new * KT + o_new * CPR * 16;
       if (lane < D / 8) {  // key row o_new of the staged tile (XOR-swizzled) and of the cache
         Raw<16> in;
@@ -220,6 +258,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
           store_raw<8>(kslot + 8 * lane, kc);
         }
       }
+      // value rows: the lanes whose tokens lie in the new token's block store them back
+      const bool mine = !PAIR || (lane_second == (o_new >= B));
 #pragma unroll
       for (int u = 0; u < NBI; ++u) {  // (u == u_new: a static index keeps vr in registers)
         if (u != u_new) continue;
@@ -227,16 +267,17 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 #pragma unroll
           for (int mi = 0; mi < MI; ++mi)
             put_elem<EB>(vr[u][mi], o_new - 4 * q4,
-                         new_value_bits<CDT, QDT>((vnew[mi / 2] >> (16 * (mi & 1))) & 0xffffu, vs[u]));
+                         new_value_bits<CDT, QDT>((vnew[mi / 2] >> (16 * (mi & 1))) & 0xffffu, vsn));
         }
+        if (mine) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          store_raw<4 * EB>(const_cast<uint8_t*>(a.v_cache) + voffs[u] + ((16 * mi + n) * B + 4 * q4) * EB,
-                            vr[u][mi]);
+          for (int mi = 0; mi < MI; ++mi)
+            store_raw<4 * EB>(const_cast<uint8_t*>(a.v_cache) + vrow[u] + 16 * mi * B * EB, vr[u][mi]);
+        }
       }
     }
 
-    // scores of the iteration's blocks
+    // scores of the iteration's tiles
     f32x4 zt[NBI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
@@ -258,20 +299,20 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
         }
       }
     }
-    int valid[NBI];  // this lane group's tokens below L, per block (<= 0: none)
+    int valid[NBI];  // this lane group's tokens of the tile below lim (<= 0: none)
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
-      valid[u] = u / SUB < nlive ? L - ((ja + 4 * (u / SUB)) * B + 16 * (u % SUB)) - 4 * q4 : 0;
+      valid[u] = u / SUB < nlive ? lim - tile_start(ia + 4 * (u / SUB), u) - 4 * q4 : 0;
     float z[4 * NBI];
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[4 * u + i] = (i < valid[u]) ? zt[u][i] * zs[u] : neg_inf();
+      for (int i = 0; i < 4; ++i) z[4 * u + i] = (i < valid[u]) ? zt[u][i] * zs_l[u] : neg_inf();
     float tm = z[0];
 #pragma unroll
     for (int i = 1; i < 4 * NBI; ++i) tm = fmaxf(tm, z[i]);
     tm = pair32_max(pair16_max(tm));
-    const float mn = fmaxf(m, tm);  // finite: every block of the sequence holds a valid token
+    const float mn = fmaxf(m, tm);  // finite: the iteration's first item starts below lim
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float pz[4 * NBI];
     float psum = 0.0f;
@@ -295,7 +336,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
       uint32_t hbits[8], lbits[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pv = pz[4 * u0 + i] * (i < 4 ? vs[u0] : vs[u1]);
+        const float pv = pz[4 * u0 + i] * (i < 4 ? vs_l[u0] : vs_l[u1]);
         hbits[i] = to16<QDT>(pv);
         lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
       }
@@ -450,8 +491,10 @@ static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
 
 template <int CDT, int QDT>
 static hipError_t launch_mfma_d(const DecodeArgs& a, int D, int B, hipStream_t st) {
+  if (D == 64 && B == 8) return launch_mfma_dnb<CDT, QDT, 64, 8>(a, st);
   if (D == 64 && B == 16) return launch_mfma_dnb<CDT, QDT, 64, 16>(a, st);
   if (D == 64 && B == 32) return launch_mfma_dnb<CDT, QDT, 64, 32>(a, st);
+  if (D == 128 && B == 8) return launch_mfma_dnb<CDT, QDT, 128, 8>(a, st);
   if (D == 128 && B == 16) return launch_mfma_dnb<CDT, QDT, 128, 16>(a, st);
   if (D == 128 && B == 32) return launch_mfma_dnb<CDT, QDT, 128, 32>(a, st);
   return hipErrorInvalidValue;
@@ -473,7 +516,7 @@ int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S, bool stream
   if (cdt == C && qdt == Q && D == DD && B == BB)                                                   \
     k = stream_kv ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, true>) \
                   : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, false>);
-#define PA_PICK_B(C, Q, DD) PA_PICK(C, Q, DD, 16) PA_PICK(C, Q, DD, 32)
+#define PA_PICK_B(C, Q, DD) PA_PICK(C, Q, DD, 8) PA_PICK(C, Q, DD, 16) PA_PICK(C, Q, DD, 32)
   PA_PICK_B(DT_F16, DT_F16, 64) PA_PICK_B(DT_F16, DT_F16, 128) PA_PICK_B(DT_BF16, DT_BF16, 64)
   PA_PICK_B(DT_BF16, DT_BF16, 128) PA_PICK_B(DT_FP8, DT_F16, 64) PA_PICK_B(DT_FP8, DT_F16, 128)
   PA_PICK_B(DT_FP8, DT_BF16, 64) PA_PICK_B(DT_FP8, DT_BF16, 128)

@@ -348,7 +348,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   const int G = num_heads / num_kv_heads;
-  const bool mfma_ok = cache_dtype != PA_F32 && (block_size == 16 || block_size == 32) && G <= 16;
+  const bool mfma_ok = cache_dtype != PA_F32 && G <= 16;  // block sizes 8, 16 and 32
   bool use_mfma;
   if (variant == PA_VARIANT_MFMA) {
     if (!mfma_ok) return PA_ERR_UNSUPPORTED;

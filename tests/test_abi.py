@@ -102,7 +102,7 @@ def _decode(L, **kw):
     (dict(qdt=F16, cdt=BF16, odt=F16), UNSUPPORTED), (dict(qdt=F32, cdt=FP8, odt=F32), UNSUPPORTED),
     (dict(odt=F16), UNSUPPORTED), (dict(cdt=FP8), INVALID),           # fp8 without scales
     (dict(cdt=F32, qdt=F32, odt=F32, variant=2), UNSUPPORTED),        # no fp32 MFMA variant
-    (dict(B=8, variant=2), UNSUPPORTED), (dict(Hq=64, Hkv=2, variant=2), UNSUPPORTED),
+    (dict(Hq=64, Hkv=2, variant=2), UNSUPPORTED),
     (dict(MB=128, part=512), WORKSPACE),                              # 4 partitions need workspace
     (dict(MB=128, part=512, ws=FAKE, wsb=100), WORKSPACE),
     (dict(S=70000), UNSUPPORTED),

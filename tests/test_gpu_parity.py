@@ -178,7 +178,8 @@ COMBOS = [
     ("bf16", "bf16", 32, 2, 128, 16, 2), ("bf16", "bf16", 4, 4, 128, 16, 2), ("f16", "f16", 6, 3, 128, 16, 0),
     ("fp8", "bf16", 8, 2, 128, 16, 2), ("fp8", "f16", 8, 2, 64, 16, 2), ("fp8", "bf16", 4, 4, 128, 16, 1),
     ("fp8", "f16", 4, 2, 128, 32, 1), ("bf16", "bf16", 8, 2, 128, 32, 2), ("f16", "f16", 4, 4, 64, 32, 2),
-    ("fp8", "bf16", 8, 1, 128, 32, 2), ("fp8", "f16", 4, 4, 64, 32, 2),
+    ("fp8", "bf16", 8, 1, 128, 32, 2), ("fp8", "f16", 4, 4, 64, 32, 2), ("bf16", "bf16", 8, 2, 128, 8, 2),
+    ("f16", "f16", 4, 4, 64, 8, 2), ("fp8", "bf16", 8, 1, 128, 8, 2), ("fp8", "f16", 4, 2, 64, 8, 2),
 ]
 
 
@@ -198,7 +199,7 @@ def test_small_parity(cdt, qdt, hq, hkv, D, B, variant, part):
 
 @pytest.mark.parametrize("lens", [[8192 + 5], [1, 0, 5000, 17, 3000, 16, 0, 2049], [40] * 1100],
                          ids=["one-long", "mixed-with-empty", "many-units"])
-@pytest.mark.parametrize("cdt,B", [("bf16", 16), ("fp8", 16), ("bf16", 32), ("fp8", 32)])
+@pytest.mark.parametrize("cdt,B", [("bf16", 16), ("fp8", 16), ("bf16", 32), ("fp8", 32), ("bf16", 8), ("fp8", 8)])
 def test_balanced_split_cuts_units(lens, cdt, B):
     """On batches of few (sequence, kv head) units the MFMA kernel's default plan spreads the K/V
     evenly over one resident grid: a lone long unit is cut across many work-groups, and empty
@@ -230,6 +231,24 @@ def test_separate_write_and_decode_parity(cdt, qdt, hq, hkv, D, B, variant, part
     assert np.array_equal(sep, fus)
     for a, b in ((ds.k_cache, df.k_cache), (ds.v_cache, df.v_cache)):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("part", [8, 24, 40, 0])
+@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
+def test_mfma_block_pairs_cut_by_partition_ends(part, cdt):
+    """At block size 8 the MFMA kernel takes pairs of blocks as one 16-token tile. Partitions of an
+    odd number of blocks (8, 24, 40 tokens) cut pairs, and the tokens of a pair's second block
+    then belong to the next partition: oracle parity, and the fused step bit for bit equal to the
+    separate write + decode."""
+    lens = [1, 7, 8, 9, 16, 23, 24, 25, 41, 100, 333, 1000]
+    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, block_size=8, dtype=cdt,
+                      q_dtype="bf16", seed=part + 5)
+    sep, ds = run_gpu(w, out_dt="f32", part=part, variant=2, return_pools=True, fused=False)
+    assert_close(sep, run_oracle(w), cdt, "f32", f"B=8 MFMA part={part}")
+    fus, df = run_gpu(w, out_dt="f32", part=part, variant=2, return_pools=True, fused=True)
+    assert np.array_equal(sep, fus)
+    for x, y in ((ds.k_cache, df.k_cache), (ds.v_cache, df.v_cache)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
 @pytest.mark.parametrize("variant", [1, 2])
