@@ -54,6 +54,8 @@ def parse_args():
                         "instead of pa_write_kv + pa_decode")
     p.add_argument("--num-seqs", type=int, default=0,
                    help="configs 2, 3, 5: use only this many sequences (a smaller batch)")
+    p.add_argument("--block-size", type=int, default=0,
+                   help="--measure prefill: block size of the cache (0 = 16)")
     p.add_argument("--measure", default="step", choices=("step", "swap", "paging", "prefill"),
                    help="step: the decode-step line (default); swap: block swap to and from pinned "
                         "host memory; paging: paged vs contiguous placement and block sizes; "
@@ -163,7 +165,7 @@ def measure_prefill(args, lib, torch):
     rng = np.random.default_rng(15)
     ctx = rng.integers(0, 3584, endpoint=True, size=16)
     w = make_prefill(ctx, [512] * 16, num_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
-                     seed=15)
+                     block_size=args.block_size or 16, seed=15)
     reps = [upload(w) for _ in range(max(1, args.replicas))]
     qs = torch.from_numpy(np.ascontiguousarray(w.query_start, dtype=np.int32)).cuda()
     T = w.q.shape[0]
@@ -202,7 +204,7 @@ def measure_prefill(args, lib, torch):
         "new_tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "config": {"workload": "prefill-16x512-gqa-bf16", "num_seqs": 16, "chunk": 512,
                    "context": "U[0,3584]", "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
-                   "block_size": 16, "new_tokens": T, "causal_pairs": w.attended_pairs(),
+                   "block_size": w.block_size, "new_tokens": T, "causal_pairs": w.attended_pairs(),
                    "flops": flops, "bytes": w.prefill_bytes()},
         "kernels_us": {"prefill": round(1e3 * k_ms, 2),
                        "write_kv": round(1e3 * w_ms / max(w_n, 1), 2)},

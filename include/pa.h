@@ -215,7 +215,7 @@ int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
  *                 whose keys and values must already be written (pa_write_kv); query row k of s
  *                 (0-based) sits at position context_lens[s] - n_s + k.
  *   max_query_len host int >= every n_s (rows beyond it are not computed).
- *   block_tables, k_cache, v_cache, scales, dtypes: as for pa_decode; block_size must be 16 and
+ *   block_tables, k_cache, v_cache, scales, dtypes: as for pa_decode (block_size 8, 16 or 32);
  *   the cache 16-bit or fp8 (matrix-core kernel). Rows of a sequence with n_s > context_lens[s]
  *   are cut to the last context_lens[s]. num_tokens == 0 is a no-op. No workspace.
  */

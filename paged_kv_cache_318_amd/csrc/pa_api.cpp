@@ -477,7 +477,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   if (max_query_len <= 0) return PA_ERR_INVALID_ARG;
-  if (!head_dim_ok(head_dim) || block_size != 16) return PA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   const bool pair_ok = ((cache_dtype == PA_F16 || cache_dtype == PA_BF16) && q_dtype == cache_dtype) ||
                        (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
   if (!pair_ok) return PA_ERR_UNSUPPORTED;
@@ -509,7 +509,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;
   const bool timed = begin_event(st, &ev);
-  const hipError_t e = pa::launch_prefill(a, cache_dtype, q_dtype, head_dim, max_query_len, st);
+  const hipError_t e = pa::launch_prefill(a, cache_dtype, q_dtype, head_dim, block_size, max_query_len, st);
   end_event(timed, st, ev, PA_KERNEL_PREFILL);
   return hip_status(e);
 }

@@ -41,8 +41,8 @@ constexpr int prefill_rows() { return 64 * prefill_column_sets<CDT, D>(); }  // 
 // its own issue and latency, not by the loads), so the ring stays at the smallest.
 constexpr int kPrefillStages = 2;
 
-// Bytes of one stage: the key tiles of two blocks, their value tiles and, for fp8 caches, 256
-// bytes whose first 16 hold the two blocks' key and value scales.
+// Bytes of one stage: the key tiles of an iteration's two 16-token tiles, their value tiles and,
+// for fp8 caches, 256 bytes whose first 32 hold the key and value scales of its (up to 4) blocks.
 template <int CDT, int D>
 constexpr size_t prefill_stage_bytes() {
   return size_t{4} * 16 * D * Elem<CDT>::bytes + (CDT == DT_FP8 ? 256 : 0);
@@ -55,16 +55,18 @@ constexpr size_t prefill_lds_bytes() {
 
 // Two column sets: 2 wave64s per SIMD (at most 256 registers a lane). One set (fp8, D = 128):
 // also 2, for the registers of its converted operands.
-template <int CDT, int QDT, int D>
+template <int CDT, int QDT, int D, int B>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int B = 16;
+  static_assert(B == 8 || B == 16 || B == 32, "block size");
+  constexpr int NBL = 32 / B;                // blocks an iteration (32 tokens) touches
   constexpr int CW = prefill_column_sets<CDT, D>();
   constexpr int ROWS = prefill_rows<CDT, D>();
   constexpr int EB = Elem<CDT>::bytes;
-  constexpr int KK = D / 32;                 // score MFMAs per block
+  constexpr int KK = D / 32;                 // score MFMAs per 16-token tile
   constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
-  constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per block
-  constexpr int KT = B * D * EB;             // bytes of one key (or value) tile
+  constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per tile
+  constexpr int KT = 16 * D * EB;            // bytes of one 16-token key (or value) tile in LDS
+  constexpr int KTB = B * D * EB;            // bytes of one (block, kv head) tile in the cache
   constexpr int CPR = D * EB / 16;           // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;              // key rows per 1 KB load
   constexpr int NCH = KT / 1024;             // 1 KB loads per tile
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int r0 = tile * ROWS;
   if (r0 >= rows) return;
   const int rlast = (r0 + ROWS < rows ? r0 + ROWS : rows) - 1;
-  const int nblk = (L - ns + rlast / G) / B + 1;   // blocks up to the group's last query
+  const int ntok = L - ns + rlast / G + 1;         // tokens up to the group's last query
+  const int nblk = (ntok + B - 1) / B;
 
   // this lane's columns: row r = (token k of the chunk, head hh of the group) of set c; rows past
   // the chunk attend token 0 only (finite, discarded)
@@ -118,40 +121,52 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int wave_min_pos = wrow + 16 * CW - 1 < rows ? L - ns + wrow / G : 0;
 
 
-  // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: tile c / NCH (0, 1: keys of
-  // blocks A, B; 2, 3: their values), part c % NCH of it.
-  // LDS buffer: keys of blocks A and B ([2][KT], rows XOR-swizzled), then their values. 16-bit
-  // values are stored per 16-row group mi as 1 KB: [block A, B][half][row] of 16-byte halves of
-  // the stored [row][16 tokens] rows. The value-operand read of lane (q4, n) (row n, tokens
-  // 4*q4 .. 4*q4+3) then covers 512 contiguous bytes per block, each 8-byte piece once (no bank
-  // conflicts; the stored [row][half] order puts rows n and n+8 on the same banks), and its two
-  // 8-byte pieces (block A, block B) sit 512 bytes apart: one paired read fills the operand.
-  // fp8 values keep the stored [row][16 tokens] order (16-byte rows read without conflicts).
-  // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: c < 2*NCH are keys (block
-  // c / NCH, part c % NCH of its tile); the rest are values (16-bit: group mi = c - 2*NCH, lanes
-  // 0-31 block A, 32-63 block B; fp8: block (c - 2*NCH) / NCH, part (c - 2*NCH) % NCH).
-  int ld_dst[NCH], ld_src[NCH];
-  bool ld_key[NCH], ld_b[NCH];
+  // Load c (c = wave + 4*i) of the iteration's 4*NCH 1 KB loads: c < 2*NCH are keys (tile
+  // c / NCH, part c % NCH of it), the rest values. An iteration covers 32 tokens: tile A (tokens
+  // 0-15) and tile B (16-31), read from the NBL blocks they lie in; each lane's 16-byte piece
+  // comes from block ld_blk of the iteration, at offset ld_src inside that block's tile.
+  // LDS stage: keys of tiles A and B ([2][KT], rows XOR-swizzled), then their values. 16-bit
+  // values are stored per 16-row group mi as 1 KB: [tile A, B][half][row] of 16-byte halves (8
+  // tokens) of the [row][16 tokens] rows. The value-operand read of lane (q4, n) (row n, tokens
+  // 4*q4 .. 4*q4+3) then covers 512 contiguous bytes per tile, each 8-byte piece once (no bank
+  // conflicts; the [row][half] order would put rows n and n+8 on the same banks), and its two
+  // 8-byte pieces (tile A, tile B) sit 512 bytes apart: one paired read fills the operand.
+  // fp8 values: [row][16 tokens] per tile (16-byte rows read without conflicts); at B = 8 a
+  // tile's 16 tokens span two blocks, so each block's [D][8] tile is staged as it is stored
+  // ([half][row][8 tokens]: a 16-byte piece is two consecutive rows of one block).
+  // Value loads: 16-bit, group mi = c - 2*NCH, lanes 0-31 tile A, 32-63 tile B; fp8, tile
+  // (c - 2*NCH) / NCH, part (c - 2*NCH) % NCH.
+  int ld_dst[NCH], ld_src[NCH], ld_blk[NCH];
+  bool ld_key[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = wave + 4 * i;
     ld_key[i] = c < 2 * NCH;
     if (c < 2 * NCH) {  // keys: lane fetches chunk (lane % CPR) ^ (row % CPR) of its row
-      const int part = c % NCH;
+      const int t = c / NCH, part = c % NCH;
       const int row = RPI * part + lane / CPR;
-      ld_b[i] = c >= NCH;
-      ld_src[i] = row * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
-      ld_dst[i] = (c / NCH) * KT + 1024 * part;
+      const int tok = 16 * t + row;
+      ld_blk[i] = tok / B;
+      ld_src[i] = (tok % B) * CPR * 16 + 16 * ((lane % CPR) ^ (row % CPR));
+      ld_dst[i] = t * KT + 1024 * part;
     } else if constexpr (EB == 2) {
-      const int mi = c - 2 * NCH, hf = (lane % 32) / 16, row = 16 * mi + lane % 16;
-      ld_b[i] = lane >= 32;
-      ld_src[i] = row * 32 + hf * 16;
+      const int mi = c - 2 * NCH, t = lane / 32, hf = (lane % 32) / 16, row = 16 * mi + lane % 16;
+      const int tok = 16 * t + 8 * hf;
+      ld_blk[i] = tok / B;
+      ld_src[i] = (row * B + tok % B) * EB;
       ld_dst[i] = 2 * KT + 1024 * mi;
     } else {
-      const int v = c - 2 * NCH;
-      ld_b[i] = v >= NCH;
-      ld_src[i] = (v % NCH) * 1024 + 16 * lane;
-      ld_dst[i] = 2 * KT + (v / NCH) * KT + 1024 * (v % NCH);
+      const int v = c - 2 * NCH, t = v / NCH, part = v % NCH;
+      ld_dst[i] = 2 * KT + t * KT + 1024 * part;
+      if constexpr (B >= 16) {
+        const int row = part * 64 + lane;
+        ld_blk[i] = (16 * t) / B;
+        ld_src[i] = row * B + (16 * t) % B;
+      } else {
+        const int q = part * 1024 + 16 * lane;  // byte of the tile's [half][row][8] stage
+        ld_blk[i] = 2 * t + q / (8 * D);
+        ld_src[i] = q % (8 * D);
+      }
     }
   }
   int kread[KL];
@@ -168,40 +183,51 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     lsum[c] = 0.0f;
   }
 
-  // Iteration i covers blocks 2i and 2i+1 (the second may lie past the group's last query).
+  // Iteration i covers tokens 32i .. 32i+31 (tile B may lie past the group's last query).
   // Its tiles go to LDS buffer i % NS: the loads for i+NS-1 are issued right after the barrier
   // that opens iteration i (every wave is then done with buffer (i-1) % NS), so NS-1 iterations
   // of loads fly while iteration i computes.
   const int32_t* trow = a.tables + static_cast<size_t>(s) * a.max_blocks;
-  const int niter = (nblk + 1) / 2;
+  const int niter = (ntok + 31) / 32;
   int tv = 0, tbase = -64;
   auto issue = [&](int it) {
-    const int j0 = 2 * it;
-    if (j0 - tbase >= 64) {  // next 64 table entries into one VGPR, read back with readlane
-      tbase = j0;
+    const int jb0 = NBL * it;  // the iteration's first block
+    if (jb0 - tbase >= 64) {  // next 64 table entries into one VGPR, read back with readlane
+      tbase = jb0;
       tv = 0;
       if (tbase + lane < nblk) {
         tv = trow[tbase + lane];
         tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
       }
     }
-    const int pba = __builtin_amdgcn_readlane(tv, j0 - tbase);
-    const int pbb = j0 + 1 < nblk ? __builtin_amdgcn_readlane(tv, j0 + 1 - tbase) : pba;
-    const size_t offa = (static_cast<size_t>(pba) * Hkv + g) * KT;
-    const size_t offb = (static_cast<size_t>(pbb) * Hkv + g) * KT;
+    // blocks past the group's last query stand in as the iteration's first: their tokens are
+    // masked, but their scales multiply zero weights, so they must be those of a block in use
+    int pb[NBL];
+    pb[0] = __builtin_amdgcn_readlane(tv, jb0 - tbase);
+#pragma unroll
+    for (int k = 1; k < NBL; ++k)
+      pb[k] = jb0 + k < nblk ? __builtin_amdgcn_readlane(tv, jb0 + k - tbase) : pb[0];
     uint8_t* buf = kt + (it % NS) * SB;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const uint8_t* src = (ld_key[i] ? a.k_cache : a.v_cache) + (ld_b[i] ? offb : offa) + ld_src[i];
+      int p = pb[0];
+#pragma unroll
+      for (int k = 1; k < NBL; ++k) p = ld_blk[i] == k ? pb[k] : p;
+      const uint8_t* src = (ld_key[i] ? a.k_cache : a.v_cache) +
+                           (static_cast<size_t>(p) * Hkv + g) * KTB + ld_src[i];
       dma16<0>(src, buf + ld_dst[i]);
     }
     if constexpr (CDT == DT_FP8) {
-      // 4 bytes a lane into the stage's scale slot: lane l holds (k A, k B, v A, v B)[l % 4]
-      // (every wave writes the same values; each issues it, so all count the same loads)
-      const float* sp = (lane & 2) ? a.v_scale : a.k_scale;
-      __builtin_amdgcn_global_load_lds(
-          (gbl_void_t*)(sp + static_cast<size_t>((lane & 1) ? pbb : pba) * Hkv + g),
-          (lds_void_t*)(buf + 4 * KT), 4, 0, 0);
+      // 4 bytes a lane into the stage's scale slot: lane l holds the key scale of block l % 8
+      // for l % 8 < NBL, the value scale of block l % 8 - 4 for 4 <= l % 8 < 4 + NBL (every wave
+      // writes the same values; each issues it, so all count the same loads)
+      const int w8 = lane % 8, k = w8 % 4;
+      int p = pb[0];
+#pragma unroll
+      for (int kk = 1; kk < NBL; ++kk) p = (k < NBL && k == kk) ? pb[kk] : p;
+      const float* sp = w8 >= 4 ? a.v_scale : a.k_scale;
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(sp + static_cast<size_t>(p) * Hkv + g),
+                                       (lds_void_t*)(buf + 4 * KT), 4, 0, 0);
     }
   };
 #pragma unroll
@@ -225,8 +251,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   for (int it = 0; it < niter; ++it) {
-    const int j0 = 2 * it;
-    const bool has_b = j0 + 1 < nblk;
+    const int t0a = 32 * it;           // first token of tile A
+    const bool has_b = t0a + 16 < ntok;
     const int slot = it % NS;
     // This wave's loads for iteration it have landed: the vector-memory counter is down to the
     // loads of the iterations issued after it (all of them near the end, when fewer are left)
@@ -242,13 +268,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     asm volatile("" ::: "memory");
     const uint8_t* kb0 = kt + slot * SB;
     const uint8_t* vt = kb0 + 2 * KT;
+    // key and value scales of this lane's tokens of tiles A and B (block (16u + 4*q4) / B)
     float zs[2] = {a.zscale, a.zscale}, vs[2] = {1.0f, 1.0f};
     if constexpr (CDT == DT_FP8) {
       const float* scl = reinterpret_cast<const float*>(kb0 + 4 * KT);
-      zs[0] *= scl[0];
-      zs[1] *= scl[1];
-      vs[0] = scl[2];
-      vs[1] = scl[3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int bi = (16 * u + 4 * q4) / B;
+        zs[u] *= scl[bi];
+        vs[u] = scl[4 + bi];
+      }
     }
     if (it + NS - 1 < niter) issue(it + NS - 1);
 
@@ -280,17 +309,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
     // Interior iterations (every token of both blocks at or before the wave's earliest query,
     // so every token is also below L) need neither the causal nor the end-of-sequence mask.
-    const bool interior = (j0 + 2) * B - 1 <= wave_min_pos;
+    const bool interior = t0a + 31 <= wave_min_pos;
     auto step = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      // per column set: online softmax of lane (q4, n)'s tokens t0(u) .. t0(u)+3 of block j0+u
+      // per column set: online softmax of lane (q4, n)'s tokens t0(u) .. t0(u)+3 of tile u
       u32x4 phi[CW], plo[CW];
 #pragma unroll
       for (int c = 0; c < CW; ++c) {
         float z[8];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int t0 = (j0 + u) * B + 4 * q4;
+          const int t0 = t0a + 16 * u + 4 * q4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if constexpr (MASKED)
@@ -334,8 +363,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       // written) get zero values
       uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
       if constexpr (MASKED) {
-        const int va = L - j0 * B - 4 * q4;                   // this lane group's tokens below L
-        const int vb = has_b ? L - (j0 + 1) * B - 4 * q4 : 0;
+        const int va = L - t0a - 4 * q4;                      // this lane group's tokens below L
+        const int vb = has_b ? L - t0a - 16 - 4 * q4 : 0;
         ma0 = va >= 2 ? 0xffffffffu : (va == 1 ? 0x0000ffffu : 0u);
         ma1 = va >= 4 ? 0xffffffffu : (va == 3 ? 0x0000ffffu : 0u);
         mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
@@ -353,7 +382,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           c0 = y.x;
           c1 = y.y;
         } else {
-          const int voff = (16 * mi + n) * B + 4 * q4;
+          const int voff = B >= 16 ? (16 * mi + n) * 16 + 4 * q4
+                                   : (q4 / 2) * (8 * D) + (16 * mi + n) * 8 + 4 * (q4 % 2);
           const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
           const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
           a0 = fp8x2_to16<QDT, false>(x);
@@ -402,30 +432,38 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-template <int CDT, int QDT, int D>
-static hipError_t launch_prefill_dn(const PrefillArgs& a, int max_query_len, hipStream_t st) {
+template <int CDT, int QDT, int D, int B>
+static hipError_t launch_prefill_dnb(const PrefillArgs& a, int max_query_len, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
   const long long rows = static_cast<long long>(max_query_len) * G;
   constexpr int R = prefill_rows<CDT, D>();
   const dim3 grid(static_cast<unsigned>((rows + R - 1) / R), a.num_kv_heads, a.num_seqs);
   const size_t shm = prefill_lds_bytes<CDT, D>();
-  hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D>), grid, dim3(256), shm, st, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D, B>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
 }
 
-template <int CDT, int QDT>
-static hipError_t launch_prefill_d(const PrefillArgs& a, int D, int max_query_len, hipStream_t st) {
-  if (D == 64) return launch_prefill_dn<CDT, QDT, 64>(a, max_query_len, st);
-  if (D == 128) return launch_prefill_dn<CDT, QDT, 128>(a, max_query_len, st);
+template <int CDT, int QDT, int D>
+static hipError_t launch_prefill_dn(const PrefillArgs& a, int B, int max_query_len, hipStream_t st) {
+  if (B == 8) return launch_prefill_dnb<CDT, QDT, D, 8>(a, max_query_len, st);
+  if (B == 16) return launch_prefill_dnb<CDT, QDT, D, 16>(a, max_query_len, st);
+  if (B == 32) return launch_prefill_dnb<CDT, QDT, D, 32>(a, max_query_len, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int cdt, int qdt, int D, int max_query_len,
+template <int CDT, int QDT>
+static hipError_t launch_prefill_d(const PrefillArgs& a, int D, int B, int max_query_len, hipStream_t st) {
+  if (D == 64) return launch_prefill_dn<CDT, QDT, 64>(a, B, max_query_len, st);
+  if (D == 128) return launch_prefill_dn<CDT, QDT, 128>(a, B, max_query_len, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int cdt, int qdt, int D, int B, int max_query_len,
                           hipStream_t st) {
-  if (cdt == DT_F16 && qdt == DT_F16) return launch_prefill_d<DT_F16, DT_F16>(a, D, max_query_len, st);
-  if (cdt == DT_BF16 && qdt == DT_BF16) return launch_prefill_d<DT_BF16, DT_BF16>(a, D, max_query_len, st);
-  if (cdt == DT_FP8 && qdt == DT_F16) return launch_prefill_d<DT_FP8, DT_F16>(a, D, max_query_len, st);
-  if (cdt == DT_FP8 && qdt == DT_BF16) return launch_prefill_d<DT_FP8, DT_BF16>(a, D, max_query_len, st);
+  if (cdt == DT_F16 && qdt == DT_F16) return launch_prefill_d<DT_F16, DT_F16>(a, D, B, max_query_len, st);
+  if (cdt == DT_BF16 && qdt == DT_BF16) return launch_prefill_d<DT_BF16, DT_BF16>(a, D, B, max_query_len, st);
+  if (cdt == DT_FP8 && qdt == DT_F16) return launch_prefill_d<DT_FP8, DT_F16>(a, D, B, max_query_len, st);
+  if (cdt == DT_FP8 && qdt == DT_BF16) return launch_prefill_d<DT_FP8, DT_BF16>(a, D, B, max_query_len, st);
   return hipErrorInvalidValue;
 }
 

@@ -204,7 +204,8 @@ def _prefill(L, **kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(S=0), INVALID), (dict(T=-1), INVALID), (dict(Hkv=3), INVALID), (dict(mql=0), INVALID),
     (dict(scale=float("inf")), INVALID), (dict(qdt=9), INVALID), (dict(NB=1 << 27), INVALID),
-    (dict(B=8), UNSUPPORTED), (dict(D=96), UNSUPPORTED), (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),
+    (dict(B=4), UNSUPPORTED), (dict(B=64), UNSUPPORTED), (dict(D=96), UNSUPPORTED),
+    (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),
     (dict(qdt=F16), UNSUPPORTED), (dict(odt=F16), UNSUPPORTED), (dict(cdt=FP8, qdt=FP8), UNSUPPORTED),
     (dict(S=70000), UNSUPPORTED), (dict(qs=None), INVALID), (dict(out=None), INVALID),
     (dict(cdt=FP8), INVALID), (dict(cdt=FP8, ks=FAKE), INVALID),

@@ -134,6 +134,32 @@ def test_prefill_parity(cdt, qdt, hq, hkv, D):
     assert_close(got16, ref, cdt, qdt, "16-bit output")
 
 
+@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("cdt,qdt,hq,hkv,D", [("bf16", "bf16", 8, 2, 128), ("f16", "f16", 16, 2, 64),
+                                              ("fp8", "bf16", 8, 2, 128), ("fp8", "f16", 4, 4, 64)])
+def test_prefill_parity_other_block_sizes(cdt, qdt, hq, hkv, D, B):
+    """Block sizes 8 and 32: an iteration's two 16-token tiles come from four blocks or from one;
+    fp8 at B = 8 stages each block's value tile as stored and reads per-lane scales."""
+    w = make_prefill(CTX, NEW, num_heads=hq, num_kv_heads=hkv, head_dim=D, dtype=cdt, q_dtype=qdt,
+                     block_size=B, seed=hq * 100 + D + B)
+    ref = run_oracle(w)
+    assert_close(run_gpu(w, out_dt="f32"), ref, cdt, "f32", f"{cdt}/{qdt} Hq={hq} Hkv={hkv} D={D} B={B}")
+    assert_close(run_gpu(w, out_dt=qdt), ref, cdt, qdt, f"16-bit output B={B}")
+
+
+@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_poison_invariance_other_block_sizes_bit_exact(dtype, B):
+    """Free blocks and unused slots filled with NaN or huge values change no output bit at block
+    sizes 8 and 32 either (blocks past a group's last query stand in as real ones)."""
+    outs = []
+    for poison in ("nan", "big"):
+        w = make_prefill([40, 333, 7, 0], [20, 70, 9, 45], num_heads=8, num_kv_heads=2, head_dim=128,
+                         dtype=dtype, block_size=B, seed=15, poison=poison)
+        outs.append(run_gpu(w, out_dt="f32"))
+    assert np.all(np.isfinite(outs[0])) and np.array_equal(outs[0], outs[1])
+
+
 def test_prompt_into_empty_cache_and_long_chunks():
     """Chunks as long as their sequences (several 64-row tiles per kv head, ragged last tile)."""
     w = make_prefill([0, 0, 0], [257, 64, 1], num_heads=8, num_kv_heads=2, head_dim=128,
