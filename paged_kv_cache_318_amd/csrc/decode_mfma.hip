@@ -14,16 +14,17 @@
 // Operand layouts (v_mfma_f32_16x16x32_{bf16,f16}: lane l = 16*q4 + n holds 8 elements of row
 // n of A and of column n of B, the k-range given by q4; the 16x16 result gives lane (q4, n) rows
 // 4*q4 .. 4*q4+3 of column n):
-//   * scores: A = keys (row n = token n of the block), B = queries (column n = head n of the
-//     group, zero for n >= G); lane group q4 supplies dims dim_base(q4, kk) .. +8 of both, so the
-//     contraction pairs the same dims. The result hands lane (q4, n) the scores of tokens
-//     4*q4 .. 4*q4+3 of the block for head n.
-//   * weighted values over the iteration's two blocks (32 tokens): A = V^T (row = dim
+//   * scores: A = keys (row n = token n of a 16-token tile), B = queries (column n = head n of
+//     the group, zero for n >= G); lane group q4 supplies dims dim_base(q4, kk) .. +8 of both, so
+//     the contraction pairs the same dims. The result hands lane (q4, n) the scores of tokens
+//     4*q4 .. 4*q4+3 of the tile for head n. A tile is a block (B = 16), half of one (B = 32)
+//     or a pair of blocks (B = 8).
+//   * weighted values over the iteration's two tiles (32 tokens): A = V^T (row = dim
 //     16*mi + n), B = P^T (column = head n); lane group q4 supplies tokens 4*q4 .. 4*q4+3 of
-//     block A then of block B -- exactly the scores it already holds, so no lane shuffles sit
+//     tile A then of tile B -- exactly the scores it already holds, so no lane shuffles sit
 //     between the two products (only the running max crosses the four lane groups). Values are
 //     stored dim-major in a block, so each lane's piece is one contiguous 8-byte (16-bit) or
-//     4-byte (fp8) load, and one load instruction covers 16 whole 32-byte dim rows.
+//     4-byte (fp8) load, and one load instruction covers 16 whole dim rows of the tile.
 //   * keys are staged through LDS with gfx950's direct global -> LDS loads: every load
 //     instruction reads 1 KB of the tile contiguously (whole cache lines, non-temporal) and the
 //     MFMA-layout reads come back out of an XOR-swizzled LDS copy.
@@ -326,8 +327,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
 
-    // weighted values, two blocks (32 tokens) per MFMA: k 0..3 are tokens 4*q4.. of the pair's
-    // first block, k 4..7 those of its second; P^T goes in as a 16-bit hi part and remainder.
+    // weighted values, two tiles (32 tokens) per MFMA: k 0..3 are tokens 4*q4.. of the pair's
+    // first tile, k 4..7 those of its second; P^T goes in as a 16-bit hi part and remainder.
     // Tokens at or beyond L get zero values (their weights are already 0).
 #pragma unroll
     for (int pr = 0; pr < NBI / 2; ++pr) {

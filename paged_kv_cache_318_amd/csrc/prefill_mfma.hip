@@ -13,7 +13,7 @@
 //     Z^T[16 tokens][16 rows]  = K_tile[16][D] . Q^T[D][16 rows]        (scores)
 //     O^T[D][16 rows]         += V^T[D][32 tokens] . P^T[32 tokens][16 rows]
 // so every K/V tile is fetched once per 128 rows, and every key or value operand read from LDS
-// feeds both sets. Per iteration the work-group stages two blocks' key and value tiles (16 KB at
+// feeds both sets. Per iteration the work-group stages two 16-token key and value tiles (16 KB at
 // 16 bits) in LDS with gfx950's direct global -> LDS loads (1 KB contiguous per load
 // instruction; keys XOR-swizzled by row so the MFMA-layout reads hit distinct banks), then every
 // wave runs its scores, its online softmax and its weighted values out of LDS. Each column
@@ -74,14 +74,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NS = kPrefillStages;
   constexpr int SB = static_cast<int>(prefill_stage_bytes<CDT, D>());
   // vector-memory operations one issue() makes per wave: its 1 KB loads, plus (fp8) the load of
-  // the two blocks' scales
+  // scales of the iteration's blocks
   constexpr int OPS = NCH + (CDT == DT_FP8 ? 1 : 0);
   static_assert((NS - 2) * OPS <= 63, "vmcnt field");
   // vmcnt((NS-2)*OPS) lgkmcnt(0): every load but those of the NS-2 iterations issued after
   // this one, and every LDS access
   constexpr int kWaitOldest = (((NS - 2) * OPS) & 15) | (7 << 4) | ((((NS - 2) * OPS) >> 4) << 14);
   extern __shared__ float smem[];
-  // [NS stages][keys of blocks A, B][values of blocks A, B (dim-major, as stored)][fp8 scales]
+  // [NS stages][keys of tiles A, B][values of tiles A, B (dim-major)][fp8 scales]
   uint8_t* kt = reinterpret_cast<uint8_t*>(smem);
 
   const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         phi[c] = u32x4{phw[0], phw[1], phw[2], phw[3]};
         plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
       }
-      // weighted values over the 32 tokens of the two blocks; slots at or beyond L (never
+      // weighted values over the 32 tokens of the two tiles; slots at or beyond L (never
       // written) get zero values
       uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
       if constexpr (MASKED) {
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
         mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
       }
-      // value operand of group mi: tokens 4*q4 .. 4*q4+3 of block A, then of block B
+      // value operand of group mi: tokens 4*q4 .. 4*q4+3 of tile A, then of tile B
       auto vop_of = [&](int mi) -> u32x4 {
         uint32_t a0, a1, c0, c1;
         if constexpr (EB == 2) {
