@@ -7,9 +7,10 @@
 // block) is a small dense contraction:
 //     Z^T[16 tokens][G heads]  = K_tile[16][D] . Q_g^T[D][G]        (scores)
 //     O^T[D][G]               += V_tile^T[D][16] . P^T[16][G]        (weighted values)
-// One work-group (4 wave64s) handles one (kv head, sequence, partition); wave w takes blocks
-// w, w+4, ... of the partition, two per iteration, so each K/V tile is fetched from HBM once for
-// all G heads and every wave keeps two tiles (16 KB at 16 bits) in flight.
+// One work-group (4 wave64s) handles one (kv head, sequence, partition); wave w takes work items
+// (blocks; pairs of blocks at B = 8) w, w+4, ... of the partition, two 16-token tiles per
+// iteration, so each K/V tile is fetched from HBM once for all G heads and every wave keeps two
+// tiles (16 KB at 16 bits) in flight.
 //
 // Operand layouts (v_mfma_f32_16x16x32_{bf16,f16}: lane l = 16*q4 + n holds 8 elements of row
 // n of A and of column n of B, the k-range given by q4; the 16x16 result gives lane (q4, n) rows
