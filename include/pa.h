@@ -174,6 +174,37 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_grouped -- pa_decode for a batch whose sequences share prefix blocks (parallel
+ * samples of one prompt: [Ultralytics] "シーケンス間でのブロック共有"; [Transcript] the paragraph
+ * on shared prefixes), with the shared blocks read once per group instead of once per sequence.
+ * The result is pa_decode's, up to the order of the floating-point sums (the prefix and the rest
+ * of a sequence are two parts combined by the same log-sum-exp merge as pa_decode's partitions).
+ *
+ *   group_start    device int32 [num_groups + 1]: sequences group_start[i] .. group_start[i+1]-1
+ *                  form group i (consecutive, non-decreasing, group_start[num_groups] = num_seqs).
+ *   prefix_blocks  device int32 [num_seqs]: the number of leading table entries sequence s shares
+ *                  with the other members of its group -- the same value for every member, the
+ *                  entries identical, and at most floor(context_lens[s] / block_size) (whole
+ *                  blocks every member attends; 0 = nothing shared). Values that break this give
+ *                  undefined results (never a fault), like duplicate slots elsewhere.
+ *   max_group_size host int: the largest group; max_group_size * (num_heads / num_kv_heads) <= 16
+ *                  (each member's query heads become rows of the matrix-core tile).
+ *   workspace      at least pa_decode_grouped_workspace_bytes(...) bytes (never NULL).
+ *   everything else as for pa_decode; the cache must be 16-bit or fp8 (matrix-core kernel).
+ */
+size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                         int max_blocks_per_seq, int block_size,
+                                         int partition_tokens);
+int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* group_start, const int32_t* prefix_blocks, int num_groups,
+                      int max_group_size, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                      float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                      const float* k_scale, const float* v_scale, int partition_tokens, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_append -- the slot write and the decode of one step in one pass: the same result, in
  * the cache and in `out`, as pa_write_kv(k_new, v_new, ..., slot_mapping, num_tokens = num_seqs)
  * followed by pa_decode ([Ultralytics] "ページングの仕組み": the new token goes to its slot;

@@ -41,7 +41,7 @@ from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["OutOfBlocks", "BlockPool", "CachingBlockPool", "block_hash"]
+__all__ = ["OutOfBlocks", "BlockPool", "CachingBlockPool", "block_hash", "shared_prefix_groups"]
 
 
 class OutOfBlocks(RuntimeError):
@@ -251,6 +251,45 @@ class BlockPool:
         hused = {h for h in range(self.num_host_blocks) if self.host_ref[h] > 0}
         assert not (hfree & hused) and hfree | hused == set(range(self.num_host_blocks)), \
             "host pool: a block is both free and used, or neither"
+
+
+# ------------------------------------------------------------------------------------------------
+# Groups of sequences sharing prefix blocks (input of pa_decode_grouped)
+# ------------------------------------------------------------------------------------------------
+
+def shared_prefix_groups(tables, lens, block_size: int,
+                         max_group_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Groups of consecutive sequences whose tables begin with the same physical blocks -- the
+    parallel samples of one prompt, which share its blocks by reference count ("PagedAttention",
+    Ultralytics glossary, section "シーケンス間でのブロック共有"). Greedy, in batch order: a
+    sequence joins the open group while the group has fewer than ``max_group_size`` members and
+    the sequence's table starts with at least one of the group's shared whole blocks.
+
+    Returns ``group_start`` (int32 [groups + 1]) and ``prefix_blocks`` (int32 [S]): the leading
+    table entries every member of the group shares, counting only blocks every member attends in
+    full (``len // block_size``); 0 for a sequence alone in its group."""
+    tables = np.asarray(tables)
+    lens = np.asarray(lens, dtype=np.int64)
+    S = int(lens.shape[0])
+    if max_group_size < 1:
+        raise ValueError("max_group_size must be at least 1")
+    full = np.maximum(lens, 0) // block_size
+    starts, prefix = [0], np.zeros(S, dtype=np.int32)
+    s = 0
+    while s < S:
+        common, e = int(full[s]), s + 1
+        while e < S and e - s < max_group_size:
+            n = min(common, int(full[e]))
+            same = np.flatnonzero(tables[e, :n] != tables[s, :n])
+            k = int(same[0]) if same.size else n
+            if k == 0:
+                break
+            common, e = k, e + 1
+        if e - s > 1:
+            prefix[s:e] = common
+        starts.append(e)
+        s = e
+    return np.asarray(starts, dtype=np.int32), prefix
 
 
 # ------------------------------------------------------------------------------------------------

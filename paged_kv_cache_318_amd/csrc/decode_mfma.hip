@@ -62,9 +62,14 @@ constexpr size_t mfma_lds_bytes(int G, int S, bool balanced) {
 // One segment: blocks [b0, b1) of unit (sequence s, kv head g) -- all G query heads of the group.
 // The result is either the unit's final output (the segment covers all of it) or a partial result
 // in workspace slot `slot`. Every thread of the work-group calls it (it synchronises).
+// seq0 >= 0 (pa_decode_grouped): the blocks are shared by sequences seq0, seq0 + 1, ..., read
+// through sequence s's table, and the rows (MFMA columns) are head n % G of sequence
+// seq0 + n / G for n < rows; each row's partial result goes to its own (sequence, head) slot list
+// at part `slot`. Otherwise rows = G and the rows are the G heads of sequence s.
 template <int CDT, int QDT, int D, int B, bool NT>
 __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, int s, int g, int L,
-                                             int b0, int b1, bool final_out, size_t slot) {
+                                             int b0, int b1, bool final_out, size_t slot,
+                                             int rows, int seq0) {
   constexpr int EB = Elem<CDT>::bytes;
   // Work items: one block (B >= 16: SUB = B/16 tiles of 16 tokens) or, for B = 8, a pair of
   // consecutive blocks forming one 16-token tile (key rows and value token columns 0-7 from the
@@ -110,10 +115,11 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   const int o_new = (L - 1) - tile_start(item_new, sub_new);
 
   u32x4 qop[KK];
-  if (n < G) {
+  if (n < rows) {
+    const int sq = seq0 >= 0 ? seq0 + n / G : s;
+    const int hq = g * G + (seq0 >= 0 ? n % G : n);
     const u32x4* qp = reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const uint8_t*>(a.q) +
-        ((static_cast<size_t>(s) * Hq + g * G + n) * D) * 2);
+        reinterpret_cast<const uint8_t*>(a.q) + ((static_cast<size_t>(sq) * Hq + hq) * D) * 2);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qop[kk] = qp[dim_base<EB>(q4, kk) / 8];
   } else {
@@ -378,19 +384,19 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   lsum = pair32_sum(pair16_sum(lsum));
   float* sm_m = smem;
   float* sm_l = smem + 64;
-  float* sm_o = smem + 128;  // [4 waves][G][D]
+  float* sm_o = smem + 128;  // [4 waves][rows][D]
   if (q4 == 0) {
     sm_m[wave * 16 + n] = m;
     sm_l[wave * 16 + n] = lsum;
   }
-  if (n < G) {
+  if (n < rows) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[(wave * G + n) * D + 16 * mi + 4 * q4 + i] = acc[mi][i];
+      for (int i = 0; i < 4; ++i) sm_o[(wave * rows + n) * D + 16 * mi + 4 * q4 + i] = acc[mi][i];
   }
   lds_barrier();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < rows * D; idx += 256) {
     const int nn = idx / D, d = idx - (idx / D) * D;
     float M = sm_m[nn];
 #pragma unroll
@@ -400,11 +406,15 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     for (int w = 0; w < 4; ++w) {
       const float mw = sm_m[w * 16 + nn];
       const float e = (mw == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-      num = __builtin_fmaf(e, sm_o[(w * G + nn) * D + d], num);
+      num = __builtin_fmaf(e, sm_o[(w * rows + nn) * D + d], num);
       den = __builtin_fmaf(e, sm_l[w * 16 + nn], den);
     }
     const float o = num / den;
-    if (final_out) {
+    if (seq0 >= 0) {
+      const size_t ix = (static_cast<size_t>(seq0 + nn / G) * Hq + g * G + nn % G) * a.max_parts + slot;
+      a.ws_o[ix * D + d] = o;
+      if (d == 0) a.ws_ml[ix] = make_float2(M, den);
+    } else if (final_out) {
       store_out(a.out, (static_cast<size_t>(s) * Hq + g * G + nn) * D + d, o, a.out_dtype);
     } else {
       a.ws_o[(slot * G + nn) * D + d] = o;
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   const int b1 = min(nblk, b0 + a.part_blocks);
   const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
   mfma_segment<CDT, QDT, D, B, NT>(a, smem, s, g, L, b0, b1, nparts == 1,
-                                (static_cast<size_t>(s) * a.num_kv_heads + g) * a.max_parts + p);
+                                (static_cast<size_t>(s) * a.num_kv_heads + g) * a.max_parts + p, G, -1);
 }
 
 // Balanced split: work-group i of a.nw takes tiles [i*W/nw, (i+1)*W/nw) of the flattened
@@ -469,15 +479,62 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs
     const long long seg_end = hi < uend ? hi : uend;
     const bool whole = (j == 0) && (seg_end == uend);
     mfma_segment<CDT, QDT, D, B, NT>(a, smem, s, g, lens_lds[s], j, j + static_cast<int>(seg_end - t),
-                                  whole, static_cast<size_t>(2 * i + (t == lo ? 0 : 1)));
+                                  whole, static_cast<size_t>(2 * i + (t == lo ? 0 : 1)), a.num_heads / a.num_kv_heads, -1);
     t = seg_end;
   }
   (void)EB;
 }
 
+// pa_decode_grouped: grid (kv head, group or sequence, part). Row y < num_groups: part p of the
+// prefix shared by group y -- the members' queries are the rows, so each shared tile is read once
+// for all of them. Row num_groups + s: part p of sequence s's own blocks after the prefix. Every
+// part is a partial result; the merge kernel combines a sequence's parts (prefix parts first).
+// A group's prefix is clamped to the full blocks every member attends, and a sequence's to its
+// own full blocks: both kernels take the same value when the prefixes are consistent.
+template <int CDT, int QDT, int D, int B, bool NT>
+__global__ __launch_bounds__(256, 3) void decode_mfma_grouped_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int g = blockIdx.x, y = blockIdx.y, p = blockIdx.z;
+  const int G = a.num_heads / a.num_kv_heads, S = a.num_seqs, pbk = a.part_blocks;
+  auto seq_len = [&](int s) {
+    const int L = a.lens[s];
+    return L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  };
+  if (y < a.num_groups) {
+    int gs = a.group_start[y], ge = a.group_start[y + 1];
+    gs = gs < 0 ? 0 : (gs > S ? S : gs);
+    ge = ge < gs ? gs : (ge > S ? S : ge);
+    const int m = ge - gs;
+    if (m <= 0 || m * G > 16) return;  // (the host checks the group size; trusted data beyond)
+    int pbe = a.prefix_blocks[gs];
+    for (int k = 0; k < m; ++k) pbe = min(pbe, seq_len(gs + k) / B);
+    pbe = pbe < 0 ? 0 : pbe;
+    const int b0 = p * pbk, b1 = min(pbe, b0 + pbk);
+    if (b0 >= b1) return;
+    mfma_segment<CDT, QDT, D, B, NT>(a, smem, gs, g, pbe * B, b0, b1, false, p, m * G, gs);
+    return;
+  }
+  const int s = y - a.num_groups;
+  const int L = seq_len(s), nblk = (L + B - 1) / B;
+  int pbe = a.prefix_blocks[s];
+  pbe = pbe < 0 ? 0 : (pbe > L / B ? L / B : pbe);
+  const int p1 = (pbe + pbk - 1) / pbk;
+  if (p == 0 && g == 0 && threadIdx.x == 0) a.ws_count[s] = p1 + (nblk - pbe + pbk - 1) / pbk;
+  const int b0 = pbe + p * pbk, b1 = min(nblk, b0 + pbk);
+  if (b0 >= b1) return;
+  mfma_segment<CDT, QDT, D, B, NT>(a, smem, s, g, L, b0, b1, false, p1 + p, G, s);
+}
+
 template <int CDT, int QDT, int D, int B>
 static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
+  if (a.grouped) {
+    const dim3 grid(a.num_kv_heads, a.num_groups + a.num_seqs, a.max_parts);
+    const size_t shm = mfma_lds_bytes<CDT, D>(16, 0, false);  // up to 16 rows
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+    else hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
+    return hipGetLastError();
+  }
   const size_t shm = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.balanced != 0);
   if (a.balanced) {
     const dim3 grid(a.nw);

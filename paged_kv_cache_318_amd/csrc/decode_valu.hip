@@ -262,7 +262,14 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
   size_t first_slot = 0;     // fixed partitions: slots first_slot + k
   int i0 = 0;                // balanced split: work-groups i0 .. i0 + count - 1
   bool i0_first = false;     // ... and whether the unit is work-group i0's first unit
-  if (a.balanced) {
+  if (a.grouped) {  // pa_decode_grouped: every part is a partial result, prefix parts first
+    count = a.ws_count[s];
+    if (count <= 0) {
+      store_out(a.out, orow + d, 0.0f, a.out_dtype);
+      return;
+    }
+    first_slot = (static_cast<size_t>(s) * a.num_heads + h) * a.max_parts;
+  } else if (a.balanced) {
     const int p0 = a.ws_pref[s], nb = a.ws_pref[s + 1] - p0;
     if (nb == 0) {
       store_out(a.out, orow + d, 0.0f, a.out_dtype);
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
     first_slot = (static_cast<size_t>(s) * hu + x) * a.max_parts;
   }
   auto slot_of = [&](int k) -> size_t {
-    if (!a.balanced) return first_slot + k;
+    if (a.grouped || !a.balanced) return first_slot + k;
     return k == 0 ? static_cast<size_t>(2 * i0 + (i0_first ? 0 : 1)) : static_cast<size_t>(2 * (i0 + k));
   };
   if (count <= kMergeFast) {

@@ -380,7 +380,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                                : fixed_workspace(num_seqs, num_heads, head_dim, pl);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
 
-  pa::DecodeArgs a;
+  pa::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.k_cache = static_cast<const uint8_t*>(k_cache);
@@ -429,6 +429,111 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
 }
 
 }  // namespace
+
+namespace {
+
+// Grouped decode plan: MFMA partitions (of the default length for many units, or the caller's),
+// one more part per (sequence, head) for the split between prefix and own blocks.
+Plan grouped_plan(int max_blocks_per_seq, int block_size, int partition_tokens) {
+  Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, true, kFewUnits);
+  pl.max_parts += 1;
+  return pl;
+}
+
+size_t grouped_workspace(int num_seqs, int num_heads, int head_dim, const Plan& pl) {
+  return slot_bytes(static_cast<size_t>(num_seqs) * num_heads * pl.max_parts, 1, head_dim) +
+         static_cast<size_t>(num_seqs) * sizeof(int);
+}
+
+}  // namespace
+
+size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                         int max_blocks_per_seq, int block_size,
+                                         int partition_tokens) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 || partition_tokens < 0)
+    return 0;
+  return grouped_workspace(num_seqs, num_heads, head_dim,
+                           grouped_plan(max_blocks_per_seq, block_size, partition_tokens));
+}
+
+int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* group_start, const int32_t* prefix_blocks, int num_groups,
+                      int max_group_size, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                      float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                      const float* k_scale, const float* v_scale, int partition_tokens, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || num_groups <= 0 || max_group_size <= 0 ||
+      num_groups > num_seqs)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
+  if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_INVALID_ARG;
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool pair_ok = ((cache_dtype == PA_F16 || cache_dtype == PA_BF16) && q_dtype == cache_dtype) ||
+                       (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
+  if (!pair_ok) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  const int G = num_heads / num_kv_heads;
+  if (static_cast<int64_t>(max_group_size) * G > 16) return PA_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_start ||
+      !prefix_blocks)
+    return PA_ERR_INVALID_ARG;
+  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  const Plan pl = grouped_plan(max_blocks_per_seq, block_size, partition_tokens);
+  if (static_cast<int64_t>(num_seqs) + num_groups > kMaxGridYZ || pl.max_parts > kMaxGridYZ)
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = grouped_workspace(num_seqs, num_heads, head_dim, pl);
+  if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  const size_t slots = static_cast<size_t>(num_seqs) * num_heads * pl.max_parts;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + slots * head_dim * sizeof(float));
+  a.ws_count = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + slot_bytes(slots, 1, head_dim));
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.part_blocks = pl.part_blocks;
+  a.max_parts = pl.max_parts;
+  a.out_dtype = out_dtype;
+  a.zscale = scale * pa::kLog2e;
+  a.stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0 ? 1 : 0;
+  a.heads_per_unit = 1;
+  a.grouped = 1;
+  a.num_groups = num_groups;
+  a.group_start = group_start;
+  a.prefix_blocks = prefix_blocks;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  bool timed = begin_event(st, &ev);
+  hipError_t e = pa::launch_decode_mfma(a, cache_dtype, q_dtype, head_dim, block_size, st);
+  end_event(timed, st, ev, PA_KERNEL_DECODE_PARTITION);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  timed = begin_event(st, &ev);
+  e = pa::launch_decode_merge(a, head_dim, block_size, st);
+  end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);
+  return hip_status(e);
+}
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int num_seqs,

@@ -228,6 +228,15 @@ struct DecodeArgs {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  // pa_decode_grouped: sequences group_start[i] .. group_start[i+1]-1 form group i and share
+  // their first prefix_blocks[s] table entries. Partial results then sit in one slot per
+  // (sequence, query head, part): ws_o[(s * Hq + h) * max_parts + k][D] (heads_per_unit 1), the
+  // parts being the prefix partitions followed by the sequence's own; ws_count[s] = their number.
+  int grouped;
+  int num_groups;
+  const int32_t* group_start;
+  const int32_t* prefix_blocks;
+  int* ws_count;
 };
 
 // Chunked prefill: sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q / out

@@ -41,6 +41,10 @@ _SIGS = {
     "pa_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp,
                           _sz, _vp], _i32),
+    "pa_decode_grouped_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pa_decode_grouped": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                           _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32,
+                           _vp, _sz, _vp], _i32),
     "pa_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
@@ -239,6 +243,40 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         S, Hq, Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
         _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), int(flags),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_grouped_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+                                      max_blocks_per_seq: int, block_size: int,
+                                      partition_tokens: int = 0) -> int:
+    return int(load().pa_decode_grouped_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                        max_blocks_per_seq, block_size,
+                                                        partition_tokens))
+
+
+def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
+                      prefix_blocks, max_group_size: int, scale: float, k_scale=None,
+                      v_scale=None, partition_tokens: int = 0, workspace=None, stream=None,
+                      flags: int = 0) -> None:
+    """pa_decode with the prefix blocks a group of sequences shares read once for the group:
+    ``group_start`` int32 [groups + 1] (consecutive sequences), ``prefix_blocks`` int32 [S]."""
+    import torch
+    NB, Hkv, B, D = k_cache.shape
+    S, Hq, Dq = q.shape
+    MB = block_tables.shape[1]
+    _need(Dq == D and tuple(out.shape) == (S, Hq, D), "q/out must be [S][Hq][D]")
+    _need(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [NB][Hkv][D][B]")
+    _need(all(t.dtype == torch.int32 for t in (block_tables, context_lens, group_start, prefix_blocks)),
+          "block_tables / context_lens / group_start / prefix_blocks must be int32")
+    _need(block_tables.shape[0] == S and context_lens.shape[0] == S and prefix_blocks.shape[0] == S,
+          "one table row / length / prefix per sequence")
+    _need(group_start.dim() == 1 and group_start.shape[0] >= 2, "group_start must be [groups + 1]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_grouped", load().pa_decode_grouped(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(group_start), _ptr(prefix_blocks), group_start.shape[0] - 1, int(max_group_size), S, Hq,
+        Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
+        _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(flags), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def pa_decode_append(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,

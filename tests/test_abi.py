@@ -47,7 +47,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("pa_write_kv", "pa_decode", "pa_decode_append", "pa_prefill", "pa_copy_blocks",
               "pa_gather_kv",
-              "pa_swap_blocks",
+              "pa_swap_blocks", "pa_decode_grouped", "pa_decode_grouped_workspace_bytes",
               "pa_decode_workspace_bytes", "pa_status_string"):
         assert n in names
 
@@ -109,6 +109,40 @@ def _decode(L, **kw):
 ])
 def test_decode_rejects_bad_arguments(L, kw, want):
     assert _decode(L, **kw) == want
+
+
+def _grouped(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, gs=FAKE, pref=FAKE, NG=2,
+             MG=4, S=8, Hq=8, Hkv=2, D=128, B=16, MB=8, NB=64, scale=0.125, qdt=BF16, cdt=BF16,
+             odt=BF16, ks=None, vs=None, part=0, flags=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.pa_decode_grouped(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["gs"],
+                               a["pref"], a["NG"], a["MG"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                               a["B"], a["MB"], a["NB"], a["scale"], a["qdt"], a["cdt"], a["odt"],
+                               a["ks"], a["vs"], a["part"], a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(NG=0), INVALID), (dict(NG=9), INVALID), (dict(MG=0), INVALID), (dict(S=0), INVALID),
+    (dict(Hkv=3), INVALID), (dict(scale=float("nan")), INVALID), (dict(flags=2), INVALID),
+    (dict(part=24), INVALID), (dict(gs=None), INVALID), (dict(pref=None), INVALID),
+    (dict(out=None), INVALID), (dict(cdt=FP8), INVALID),              # fp8 without scales
+    (dict(MG=5), UNSUPPORTED),                                        # 5 members x 4 heads > 16
+    (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),                   # matrix-core kernel only
+    (dict(D=96), UNSUPPORTED), (dict(B=64), UNSUPPORTED), (dict(odt=F16), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(S=70000, NG=2), UNSUPPORTED),
+])
+def test_grouped_decode_rejects_bad_arguments(L, kw, want):
+    assert _grouped(L, **kw) == want
+
+
+def test_grouped_workspace_bytes(L):
+    # one slot of D floats + (max, sum) per (sequence, head, part), parts = ceil(MB / pb) + 1, and
+    # one part count per sequence; MFMA default partitions of 1024 tokens
+    n = palib.pa_decode_grouped_workspace_bytes(8, 8, 128, 128, 16, 0)
+    assert n == 8 * 8 * (2 + 1) * (128 + 2) * 4 + 8 * 4
+    assert palib.pa_decode_grouped_workspace_bytes(8, 8, 128, 128, 16, 256) == 8 * 8 * 9 * 130 * 4 + 32
+    assert palib.pa_decode_grouped_workspace_bytes(0, 8, 128, 128, 16, 0) == 0
 
 
 def _write(L, **kw):
