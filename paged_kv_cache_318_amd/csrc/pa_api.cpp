@@ -319,22 +319,20 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
 
 namespace {
 
-// pa_decode, and pa_decode_append when k_new != nullptr (new tokens taken along and written).
-int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-                int num_heads, int num_kv_heads, int head_dim, int block_size,
-                int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
-                pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
-                const float* v_scale, int partition_tokens, int variant, int flags,
-                void* workspace, size_t workspace_bytes, void* stream, const void* k_new,
-                const void* v_new, const int32_t* slot_mapping) {
+// Checks shared by pa_decode, pa_decode_append and pa_decode_grouped: sizes, scale, dtypes,
+// flags, partition length, 32-bit slot ranges, supported shapes and dtype pairs, pointers.
+int check_decode_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                      pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                      const float* v_scale, int partition_tokens, int flags) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
-  if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
   if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_INVALID_ARG;
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
     return PA_ERR_INVALID_ARG;
@@ -347,6 +345,24 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// pa_decode, and pa_decode_append when k_new != nullptr (new tokens taken along and written).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                int num_heads, int num_kv_heads, int head_dim, int block_size,
+                int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                const float* v_scale, int partition_tokens, int variant, int flags,
+                void* workspace, size_t workspace_bytes, void* stream, const void* k_new,
+                const void* v_new, const int32_t* slot_mapping) {
+  if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
+  const int status = check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype,
+                                       out_dtype, k_scale, v_scale, partition_tokens, flags);
+  if (status != PA_OK) return status;
   const int G = num_heads / num_kv_heads;
   const bool mfma_ok = cache_dtype != PA_F32 && G <= 16;  // block sizes 8, 16 and 32
   bool use_mfma;
@@ -465,29 +481,16 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
                       float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
                       const float* k_scale, const float* v_scale, int partition_tokens, int flags,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0 || num_groups <= 0 || max_group_size <= 0 ||
-      num_groups > num_seqs)
-    return PA_ERR_INVALID_ARG;
-  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (!dtype_ok(q_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(out_dtype)) return PA_ERR_INVALID_ARG;
-  if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_INVALID_ARG;
-  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
-    return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
-  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
-  const bool pair_ok = ((cache_dtype == PA_F16 || cache_dtype == PA_BF16) && q_dtype == cache_dtype) ||
-                       (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
-  if (!pair_ok) return PA_ERR_UNSUPPORTED;
-  if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (num_groups <= 0 || max_group_size <= 0 || num_groups > num_seqs) return PA_ERR_INVALID_ARG;
+  const int status = check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype,
+                                       out_dtype, k_scale, v_scale, partition_tokens, flags);
+  if (status != PA_OK) return status;
+  if (cache_dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // the matrix-core kernel only
   const int G = num_heads / num_kv_heads;
   if (static_cast<int64_t>(max_group_size) * G > 16) return PA_ERR_UNSUPPORTED;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_start ||
-      !prefix_blocks)
-    return PA_ERR_INVALID_ARG;
-  if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (!group_start || !prefix_blocks) return PA_ERR_INVALID_ARG;
   const Plan pl = grouped_plan(max_blocks_per_seq, block_size, partition_tokens);
   if (static_cast<int64_t>(num_seqs) + num_groups > kMaxGridYZ || pl.max_parts > kMaxGridYZ)
     return PA_ERR_UNSUPPORTED;
