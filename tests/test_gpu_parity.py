@@ -122,10 +122,18 @@ def test_config1_tiny_fp32():
     assert_close(run_gpu(w, part=16), ref, "f32", "f32", "cfg1 split")
 
 
+def _bench_launch_and_fused(w, out_dt, **kw):
+    """The step as bench.py times it (pa_write_kv, then pa_decode with the default plan), and the
+    fused step (pa_decode_append), which must give the same bits."""
+    sep = run_gpu(w, out_dt=out_dt, fused=False, **kw)
+    assert np.array_equal(sep, run_gpu(w, out_dt=out_dt, fused=True, **kw))
+    return sep
+
+
 @pytest.mark.parametrize("out_dt", ["f16", "f32"])
 def test_config2_opt13b_mha_fp16(out_dt):
     w = cfg(2)
-    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(2), "f16", out_dt, "cfg2")
+    assert_close(_bench_launch_and_fused(w, out_dt), cfg_ref(2), "f16", out_dt, "cfg2")
 
 
 def test_config2_bf16_variant():
@@ -136,7 +144,7 @@ def test_config2_bf16_variant():
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 def test_config3_gqa_long_bf16(out_dt):
     w = cfg(3)
-    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(3), "bf16", out_dt, "cfg3")
+    assert_close(_bench_launch_and_fused(w, out_dt), cfg_ref(3), "bf16", out_dt, "cfg3")
 
 
 def test_config3_valu_variant_agrees():
@@ -152,6 +160,8 @@ def test_config4_shared_prefix(first_step):
         assert w.cow.shape[0] > 0
     got, d = run_gpu(w, out_dt="f32", return_pools=True, flags=lib.PA_DECODE_SHARED_BLOCKS)
     assert_close(got, cfg_ref(4, first_step=first_step), "bf16", "f32", "cfg4")
+    # the step as bench.py times it: separate write and decode, same bits
+    assert np.array_equal(run_gpu(w, out_dt="f32", flags=lib.PA_DECODE_SHARED_BLOCKS, fused=False), got)
     kp, vp, _, _ = _host_after_step(w)
     assert np.array_equal(d.k_cache.view(torch.int16).cpu().numpy().view(np.uint16), kp)
     assert np.array_equal(d.v_cache.view(torch.int16).cpu().numpy().view(np.uint16), vp)
@@ -162,7 +172,7 @@ def test_config4_shared_prefix(first_step):
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 def test_config5_fp8(out_dt):
     w = cfg(5)
-    assert_close(run_gpu(w, out_dt=out_dt), cfg_ref(5), "fp8", out_dt, "cfg5")
+    assert_close(_bench_launch_and_fused(w, out_dt), cfg_ref(5), "fp8", out_dt, "cfg5")
 
 
 # ----------------------------------------------------------------------------------------------
