@@ -147,6 +147,18 @@ def test_config3_gqa_long_bf16(out_dt):
     assert_close(_bench_launch_and_fused(w, out_dt), cfg_ref(3), "bf16", out_dt, "cfg3")
 
 
+@pytest.mark.parametrize("B", [8, 32])
+def test_config3_other_block_sizes_sampled(B):
+    """The GQA batch at its full size with blocks of 8 and 32 tokens (the MFMA kernel takes block
+    pairs and half blocks as its 16-token tiles), as bench.py times it: every 8th sequence against
+    the oracle, and the fused step bit for bit equal."""
+    w = cfg(3, block_size=B)
+    got = _bench_launch_and_fused(w, "f32")
+    seqs = list(range(0, w.num_seqs, 8))
+    ref = run_oracle(w, seqs=seqs)
+    assert_close(got[seqs], ref[seqs], "bf16", "f32", f"cfg3 B={B}")
+
+
 def test_config3_valu_variant_agrees():
     w = cfg(3)
     assert_close(run_gpu(w, out_dt="f32", variant=lib.PA_VARIANT_VALU), cfg_ref(3), "bf16", "f32",
