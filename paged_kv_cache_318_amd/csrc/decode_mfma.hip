@@ -341,17 +341,17 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     for (int pr = 0; pr < NBI / 2; ++pr) {
       if ((2 * pr) / SUB >= nlive) break;
       const int u0 = 2 * pr, u1 = 2 * pr + 1;
-      uint32_t hbits[8], lbits[8];
+      // (gfx950's packed converters, round to nearest even: two weights an instruction)
+      uint32_t phw[4], plw[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float pv = pz[4 * u0 + i] * (i < 4 ? vs_l[u0] : vs_l[u1]);
-        hbits[i] = to16<QDT>(pv);
-        lbits[i] = to16<QDT>(pv - from16<QDT>(hbits[i]));
+      for (int i = 0; i < 4; ++i) {
+        const float sc = i < 2 ? vs_l[u0] : vs_l[u1];
+        const float p0 = pz[4 * u0 + 2 * i] * sc, p1 = pz[4 * u0 + 2 * i + 1] * sc;
+        phw[i] = pack16x2<QDT>(p0, p1);
+        plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
       }
-      const u32x4 phi{hbits[0] | (hbits[1] << 16), hbits[2] | (hbits[3] << 16),
-                      hbits[4] | (hbits[5] << 16), hbits[6] | (hbits[7] << 16)};
-      const u32x4 plo{lbits[0] | (lbits[1] << 16), lbits[2] | (lbits[3] << 16),
-                      lbits[4] | (lbits[5] << 16), lbits[6] | (lbits[7] << 16)};
+      const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
+      const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};
       const uint32_t ma0 = valid[u0] >= 2 ? 0xffffffffu : (valid[u0] == 1 ? 0x0000ffffu : 0u);
       const uint32_t ma1 = valid[u0] >= 4 ? 0xffffffffu : (valid[u0] == 3 ? 0x0000ffffu : 0u);
       const uint32_t mb0 = valid[u1] >= 2 ? 0xffffffffu : (valid[u1] == 1 ? 0x0000ffffu : 0u);
