@@ -372,7 +372,7 @@ def main():
     import torch
 
     from paged_kv_cache_318_amd import lib
-    from paged_kv_cache_318_amd.step import decode_step, workspace_for
+    from paged_kv_cache_318_amd.step import decode_step, decode_step_grouped, workspace_for
     from workloads import config
     from workloads.device import torch_dtype, upload
 
@@ -425,13 +425,10 @@ def main():
     def step(i):
         d = reps[i % len(reps)]
         if grouped is not None:
-            if d.cow.shape[0] > 0:
-                lib.pa_copy_blocks(d.k_cache, d.v_cache, d.cow, d.k_scale, d.v_scale)
-            lib.pa_write_kv(d.k_new, d.v_new, d.k_cache, d.v_cache, d.slots, d.k_scale, d.v_scale)
-            lib.pa_decode_grouped(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, grouped[0],
-                                  grouped[1], grouped[2], w.scale, d.k_scale, d.v_scale,
-                                  partition_tokens=args.partition, workspace=grouped[3],
-                                  flags=flags)
+            decode_step_grouped(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new,
+                                d.slots, d.cow, grouped[0], grouped[1], grouped[2], w.scale,
+                                d.k_scale, d.v_scale, partition_tokens=args.partition,
+                                workspace=grouped[3], flags=flags)
             return
         decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
