@@ -347,8 +347,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
       for (int i = 0; i < 4; ++i) {
         const float sc = i < 2 ? vs_l[u0] : vs_l[u1];
         const float p0 = pz[4 * u0 + 2 * i] * sc, p1 = pz[4 * u0 + 2 * i + 1] * sc;
-        phw[i] = pack16x2<QDT>(p0, p1);
-        plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
+        split16x2<QDT>(p0, p1, phw[i], plw[i]);
       }
       const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
       const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};

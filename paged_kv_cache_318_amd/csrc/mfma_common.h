@@ -54,6 +54,27 @@ __device__ __forceinline__ float lo16_to_f32(uint32_t w) { return from16<QDT>(w 
 template <int QDT>
 __device__ __forceinline__ float hi16_to_f32(uint32_t w) { return from16<QDT>(w >> 16); }
 
+// (a, b) -> hi: both rounded to the 16-bit type; lo: the two rounding remainders, rounded too.
+// hi + lo carries a and b to about 16 significant bits. For bf16 each remainder is one dot2
+// instruction, hi . (-1, 0) + a and hi . (0, -1) + b: both products are exact and the remainder
+// of a rounding to bf16 is an fp32 number (bf16 has fp32's exponent range), so the sum is exact.
+template <int QDT>
+__device__ __forceinline__ void split16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack16x2<QDT>(a, b);
+  if constexpr (QDT == DT_BF16) {
+    // (-1, 0) goes through a scalar register: as an operand of this instruction the compiler
+    // encodes it as the inline constant -1.0, which the hardware does not read as that pair
+    uint32_t m1_lo;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(m1_lo));
+    const bf16x2_t h = __builtin_bit_cast(bf16x2_t, hi);
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, m1_lo), a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, 0xbf800000u), b, false);
+    lo = pack16x2<QDT>(ra, rb);
+  } else {
+    lo = pack16x2<QDT>(a - lo16_to_f32<QDT>(hi), b - hi16_to_f32<QDT>(hi));
+  }
+}
+
 // First of the 8 contiguous dims lane group q4 contributes to score MFMA kk: 16-bit keys load
 // 16 bytes (8 dims) per MFMA at byte 64*kk + 16*q4 of the row; fp8 keys load 16 bytes (16 dims,
 // two MFMAs) at byte 64*(kk/2) + 16*q4.
@@ -77,11 +98,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 // trip as with a lane shuffle. max and + are commutative, so the order does not matter.
 __device__ __forceinline__ float pair16_max(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+  return a > b ? a : b;
 }
 __device__ __forceinline__ float pair32_max(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+  return a > b ? a : b;
 }
 __device__ __forceinline__ float pair16_sum(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -250,7 +250,22 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  for (int it = 0; it < niter; ++it) {
+  // 16-bit caches scale every score by one factor, zsp = |scale * log2(e)|: a negative scale
+  // goes into the query's sign bits (exact), so that the running max can be taken on the
+  // unscaled scores and the factor applied inside the exponent's FMA
+  const float zsp = EB == 2 ? fabsf(a.zscale) : a.zscale;
+  if constexpr (EB == 2) {
+    if (a.zscale < 0.0f) {
+#pragma unroll
+      for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          qop[c][kk] = u32x4{qop[c][kk].x ^ 0x80008000u, qop[c][kk].y ^ 0x80008000u,
+                             qop[c][kk].z ^ 0x80008000u, qop[c][kk].w ^ 0x80008000u};
+    }
+  }
+  auto body = [&](const int it, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int t0a = 32 * it;           // first token of tile A
     const bool has_b = t0a + 16 < ntok;
     const int slot = it % NS;
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     const uint8_t* kb0 = kt + slot * SB;
     const uint8_t* vt = kb0 + 2 * KT;
     // key and value scales of this lane's tokens of tiles A and B (block (16u + 4*q4) / B)
-    float zs[2] = {a.zscale, a.zscale}, vs[2] = {1.0f, 1.0f};
+    float zs[2] = {zsp, zsp}, vs[2] = {1.0f, 1.0f};
     if constexpr (CDT == DT_FP8) {
       const float* scl = reinterpret_cast<const float*>(kb0 + 4 * KT);
 #pragma unroll
@@ -307,115 +322,129 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
-    // Interior iterations (every token of both blocks at or before the wave's earliest query,
-    // so every token is also below L) need neither the causal nor the end-of-sequence mask.
-    const bool interior = t0a + 31 <= wave_min_pos;
-    auto step = [&](auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      // per column set: online softmax of lane (q4, n)'s tokens t0(u) .. t0(u)+3 of tile u
-      u32x4 phi[CW], plo[CW];
+    // per column set: online softmax of lane (q4, n)'s tokens t0(u) .. t0(u)+3 of tile u
+    u32x4 phi[CW], plo[CW];
 #pragma unroll
-      for (int c = 0; c < CW; ++c) {
-        float z[8];
+    for (int c = 0; c < CW; ++c) {
+      // z: the scores of lane (q4, n)'s tokens, unscaled for 16-bit caches (one common factor
+      // zsp >= 0, applied in the exponent), scaled per tile for fp8; ok: inside the causal
+      // limit and (tile B) inside the group's tokens
+      float z[8];
+      bool ok[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int t0 = t0a + 16 * u + 4 * q4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (MASKED)
-              z[4 * u + i] = (t0 + i <= pos[c] && (u == 0 || has_b)) ? zt[c][u][i] * zs[u] : neg_inf();
-            else
-              z[4 * u + i] = zt[c][u][i] * zs[u];
-          }
-        }
-        float tm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-        tm = pair32_max(pair16_max(tm));
-        // The running max only moves when some column of the set sees a larger score; the
-        // accumulators are rescaled only then (the result is the same for any common shift).
-        if (__builtin_amdgcn_ballot_w64(tm > m[c]) != 0) {
-          const float mn = fmaxf(m[c], tm);  // finite: block 0 holds token 0, which every column attends
-          const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
-          lsum[c] *= alpha;
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi) acc[c][mi] = acc[c][mi] * alpha;
-          m[c] = mn;
-        }
-        float pz[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pz[i] = __builtin_amdgcn_exp2f(z[i] - m[c]);
-          lsum[c] += pz[i];
-        }
-        // P^T as 16-bit hi part + remainder
-        uint32_t phw[4], plw[4];
+      for (int u = 0; u < 2; ++u) {
+        const int t0 = t0a + 16 * u + 4 * q4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float vsc = i < 2 ? vs[0] : vs[1];
-          const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
-          phw[i] = pack16x2<QDT>(p0, p1);
-          plw[i] = pack16x2<QDT>(p0 - lo16_to_f32<QDT>(phw[i]), p1 - hi16_to_f32<QDT>(phw[i]));
+          ok[4 * u + i] = !MASKED || (t0 + i <= pos[c] && (u == 0 || has_b));
+          z[4 * u + i] = EB == 2 ? zt[c][u][i] : zt[c][u][i] * zs[u];
         }
-        phi[c] = u32x4{phw[0], phw[1], phw[2], phw[3]};
-        plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
       }
-      // weighted values over the 32 tokens of the two tiles; slots at or beyond L (never
-      // written) get zero values
-      uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
-      if constexpr (MASKED) {
-        const int va = L - t0a - 4 * q4;                      // this lane group's tokens below L
-        const int vb = has_b ? L - t0a - 16 - 4 * q4 : 0;
-        ma0 = va >= 2 ? 0xffffffffu : (va == 1 ? 0x0000ffffu : 0u);
-        ma1 = va >= 4 ? 0xffffffffu : (va == 3 ? 0x0000ffffu : 0u);
-        mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
-        mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
+      float zm[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zm[i] = ok[i] ? z[i] : neg_inf();
+      // a chain, which the compiler folds into 3-input maxes
+      float tm = zm[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tm = fmaxf(tm, zm[i]);
+      tm = pair32_max(pair16_max(tm));
+      // -inf * 0 (every token of a column masked, zero scale) is NaN: compares false below
+      if constexpr (EB == 2) tm *= zsp;
+      // The accumulators are rescaled to a new running max only when some column of the set
+      // sees a score above its max by more than kSlack (log2 units); until then its weights run
+      // up to 2^kSlack (the result is the same for any common shift, the final division takes
+      // it out). bf16 has fp32's range; fp16 weights keep the eager rescale, so that a weight
+      // times a large fp8 value scale cannot overflow.
+      constexpr float kSlack = QDT == DT_BF16 ? 8.0f : 0.0f;
+      if (__builtin_amdgcn_ballot_w64(tm > m[c] + kSlack) != 0) {
+        const float mn = fmaxf(m[c], tm);  // finite: block 0 holds token 0, which every column attends
+        const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) acc[c][mi] = acc[c][mi] * alpha;
+        m[c] = mn;
       }
-      // value operand of group mi: tokens 4*q4 .. 4*q4+3 of tile A, then of tile B
-      auto vop_of = [&](int mi) -> u32x4 {
-        uint32_t a0, a1, c0, c1;
-        if constexpr (EB == 2) {
-          const int voff = 1024 * mi + 256 * (q4 / 2) + 16 * n + 8 * (q4 % 2);
-          const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
-          const u32x2 y = *reinterpret_cast<const u32x2*>(vt + voff + 512);
-          a0 = x.x;
-          a1 = x.y;
-          c0 = y.x;
-          c1 = y.y;
-        } else {
-          const int voff = B >= 16 ? (16 * mi + n) * 16 + 4 * q4
-                                   : (q4 / 2) * (8 * D) + (16 * mi + n) * 8 + 4 * (q4 % 2);
-          const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
-          const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
-          a0 = fp8x2_to16<QDT, false>(x);
-          a1 = fp8x2_to16<QDT, true>(x);
-          c0 = fp8x2_to16<QDT, false>(y);
-          c1 = fp8x2_to16<QDT, true>(y);
-        }
-        if constexpr (MASKED) return u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
-        else return u32x4{a0, a1, c0, c1};
-      };
-      // each value operand read once from LDS and multiplied into every column set; groups of
-      // 4 value tiles (hi MFMAs of the group, then its remainder MFMAs) so no MFMA waits on the
-      // one just issued into the same accumulator
-      constexpr int GV = CW == 1 ? 4 : 2;
+      float pz[8];
 #pragma unroll
-      for (int m0 = 0; m0 < MI; m0 += GV) {
-        u32x4 vop[GV];
-#pragma unroll
-        for (int j = 0; j < GV; ++j) {
-          vop[j] = vop_of(m0 + j);
-#pragma unroll
-          for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], phi[c], acc[c][m0 + j]);
-        }
-#pragma unroll
-        for (int j = 0; j < GV; ++j)
-#pragma unroll
-          for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], plo[c], acc[c][m0 + j]);
+      for (int i = 0; i < 8; ++i) {
+        const float e = EB == 2 ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], zsp, -m[c]))
+                                : __builtin_amdgcn_exp2f(z[i] - m[c]);
+        pz[i] = ok[i] ? e : 0.0f;
+        lsum[c] += pz[i];
       }
+      // P^T as 16-bit hi part + remainder
+      uint32_t phw[4], plw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float vsc = i < 2 ? vs[0] : vs[1];
+        const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
+        split16x2<QDT>(p0, p1, phw[i], plw[i]);
+      }
+      phi[c] = u32x4{phw[0], phw[1], phw[2], phw[3]};
+      plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
+    }
+    // weighted values over the 32 tokens of the two tiles; slots at or beyond L (never
+    // written) get zero values
+    uint32_t ma0 = ~0u, ma1 = ~0u, mb0 = ~0u, mb1 = ~0u;
+    if constexpr (MASKED) {
+      const int va = L - t0a - 4 * q4;                      // this lane group's tokens below L
+      const int vb = has_b ? L - t0a - 16 - 4 * q4 : 0;
+      ma0 = va >= 2 ? 0xffffffffu : (va == 1 ? 0x0000ffffu : 0u);
+      ma1 = va >= 4 ? 0xffffffffu : (va == 3 ? 0x0000ffffu : 0u);
+      mb0 = vb >= 2 ? 0xffffffffu : (vb == 1 ? 0x0000ffffu : 0u);
+      mb1 = vb >= 4 ? 0xffffffffu : (vb == 3 ? 0x0000ffffu : 0u);
+    }
+    // value operand of group mi: tokens 4*q4 .. 4*q4+3 of tile A, then of tile B
+    auto vop_of = [&](int mi) -> u32x4 {
+      uint32_t a0, a1, c0, c1;
+      if constexpr (EB == 2) {
+        const int voff = 1024 * mi + 256 * (q4 / 2) + 16 * n + 8 * (q4 % 2);
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vt + voff);
+        const u32x2 y = *reinterpret_cast<const u32x2*>(vt + voff + 512);
+        a0 = x.x;
+        a1 = x.y;
+        c0 = y.x;
+        c1 = y.y;
+      } else {
+        const int voff = B >= 16 ? (16 * mi + n) * 16 + 4 * q4
+                                 : (q4 / 2) * (8 * D) + (16 * mi + n) * 8 + 4 * (q4 % 2);
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(vt + voff);
+        const uint32_t y = *reinterpret_cast<const uint32_t*>(vt + KT + voff);
+        a0 = fp8x2_to16<QDT, false>(x);
+        a1 = fp8x2_to16<QDT, true>(x);
+        c0 = fp8x2_to16<QDT, false>(y);
+        c1 = fp8x2_to16<QDT, true>(y);
+      }
+      if constexpr (MASKED) return u32x4{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
+      else return u32x4{a0, a1, c0, c1};
     };
-    if (interior) step(std::false_type{});
-    else step(std::true_type{});
-  }
+    // each value operand read once from LDS and multiplied into every column set; groups of
+    // 4 value tiles (hi MFMAs of the group, then its remainder MFMAs) so no MFMA waits on the
+    // one just issued into the same accumulator
+    constexpr int GV = CW == 1 ? 4 : 2;
+#pragma unroll
+    for (int m0 = 0; m0 < MI; m0 += GV) {
+      u32x4 vop[GV];
+#pragma unroll
+      for (int j = 0; j < GV; ++j) {
+        vop[j] = vop_of(m0 + j);
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], phi[c], acc[c][m0 + j]);
+      }
+#pragma unroll
+      for (int j = 0; j < GV; ++j)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], plo[c], acc[c][m0 + j]);
+    }
+  };
+  // Interior iterations (every token of both tiles at or before the wave's earliest query, so
+  // also below L) need neither the causal nor the end-of-sequence mask; they come first and run
+  // in a loop of their own. With both kinds in one loop the compiler gave the accumulators
+  // different registers on the two paths and copied all of them every iteration.
+  const int n_interior = min((wave_min_pos + 1) / 32, niter);
+  int it = 0;
+  for (; it < n_interior; ++it) body(it, std::false_type{});
+  for (; it < niter; ++it) body(it, std::true_type{});
 
 #pragma unroll
   for (int c = 0; c < CW; ++c) {

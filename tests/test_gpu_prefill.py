@@ -8,8 +8,8 @@ ulp of a 16-bit output at the reference value.
 Cases: every supported dtype pairing, group size (1, 4, 8, 16 query heads per kv head) and head
 size, chunks spanning several 64-row tiles with ragged tails, empty chunks and empty contexts,
 one-token chunks (the decode step), a chunk as long as its sequence (a prompt into an empty
-cache), NaN-poisoned unused memory, placement invariance, and a full-size chunked-prefill batch
-checked on sampled rows.
+cache), negative, zero and large scales, NaN-poisoned unused memory, placement invariance, and a
+full-size chunked-prefill batch checked on sampled rows.
 """
 
 import numpy as np
@@ -145,6 +145,19 @@ def test_prefill_parity_other_block_sizes(cdt, qdt, hq, hkv, D, B):
     ref = run_oracle(w)
     assert_close(run_gpu(w, out_dt="f32"), ref, cdt, "f32", f"{cdt}/{qdt} Hq={hq} Hkv={hkv} D={D} B={B}")
     assert_close(run_gpu(w, out_dt=qdt), ref, cdt, qdt, f"16-bit output B={B}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 2.0])
+@pytest.mark.parametrize("cdt,qdt", [("bf16", "bf16"), ("f16", "f16"), ("fp8", "bf16")])
+def test_prefill_scale_sign_and_size(cdt, qdt, scale):
+    """Any finite scale: negative (16-bit caches carry its sign in the query operand), zero (equal
+    weights: the mean of the attended values) and large (nearly one-hot weights whose running max
+    jumps by far more than the rescale slack from one tile to the next)."""
+    w = make_prefill(CTX, NEW, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype=qdt,
+                     seed=700 + int(8 * scale))
+    w.scale = scale
+    ref = run_oracle(w)
+    assert_close(run_gpu(w, out_dt="f32"), ref, cdt, "f32", f"{cdt}/{qdt} scale={scale}")
 
 
 @pytest.mark.parametrize("B", [8, 32])
