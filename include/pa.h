@@ -249,6 +249,8 @@ int pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
  *   block_tables, k_cache, v_cache, scales, dtypes: as for pa_decode (block_size 8, 16 or 32);
  *   the cache 16-bit or fp8 (matrix-core kernel). Rows of a sequence with n_s > context_lens[s]
  *   are cut to the last context_lens[s]. num_tokens == 0 is a no-op. No workspace.
+ *   PA_ERR_UNSUPPORTED when ceil(max_query_len * num_heads / num_kv_heads / 64) * num_kv_heads
+ *   * num_seqs reaches 2^31 (one work-group per 64-row tile, kv head and sequence).
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,

@@ -590,9 +590,10 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                        (cache_dtype == PA_FP8_E4M3 && (q_dtype == PA_F16 || q_dtype == PA_BF16));
   if (!pair_ok) return PA_ERR_UNSUPPORTED;
   if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
-  if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   const int G = num_heads / num_kv_heads;
-  if ((static_cast<int64_t>(max_query_len) * G + 63) / 64 >= (int64_t{1} << 31)) return PA_ERR_UNSUPPORTED;
+  // one work-group per (64-row tile, kv head, sequence), in a one-dimensional grid
+  if ((static_cast<int64_t>(max_query_len) * G + 63) / 64 * num_kv_heads * num_seqs >= (int64_t{1} << 31))
+    return PA_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;

@@ -252,6 +252,7 @@ struct PrefillArgs {
   const float* k_scale;
   const float* v_scale;
   int num_seqs, num_tokens, num_heads, num_kv_heads, max_blocks, num_blocks, out_dtype;
+  int num_tiles;   // row tiles per (sequence, kv head): the longest chunk's rows / rows per tile
   float zscale;    // softmax scale * log2(e)
 };
 

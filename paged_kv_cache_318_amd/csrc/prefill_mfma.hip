@@ -20,6 +20,7 @@
 // carries its own causal limit (its query position); a wave's rows never leave it, so no
 // cross-wave merge is needed and no workspace either.
 
+#include <climits>
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -53,6 +54,30 @@ constexpr size_t prefill_lds_bytes() {
   return size_t{kPrefillStages} * prefill_stage_bytes<CDT, D>();
 }
 
+// The sequence of rank r when the num_seqs sequences are ordered by length, longest first (ties:
+// lower index first). Lane j of the wave ranks sequences j, j + 64, ...: every work-group
+// computes the same permutation from the lengths alone. Past 256 sequences the order is the
+// sequences' own (the ranking would cost more than it saves).
+__device__ int seq_by_length_rank(const int32_t* lens, int S, int r, int lane, int maxL) {
+  if (S > 256) return r;
+  for (int j0 = 0; j0 < S; j0 += 64) {
+    const int j = j0 + lane;
+    const int kj = j < S ? min(max(lens[j], 0), maxL) : -1;
+    int rank = 0;
+    for (int i0 = 0; i0 < S; i0 += 64) {
+      const int ki_l = i0 + lane < S ? min(max(lens[i0 + lane], 0), maxL) : -1;
+      const int n = min(64, S - i0);
+      for (int t = 0; t < n; ++t) {
+        const int ki = __builtin_amdgcn_readlane(ki_l, t);
+        rank += (ki > kj || (ki == kj && i0 + t < j)) ? 1 : 0;
+      }
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(j < S && rank == r);
+    if (hit != 0) return j0 + static_cast<int>(__builtin_ctzll(hit));
+  }
+  return r;  // not reached: the ranks are a permutation of 0 .. S-1
+}
+
 // Two column sets: 2 wave64s per SIMD (at most 256 registers a lane). One set (fp8, D = 128):
 // also 2, for the registers of its converted operands.
 template <int CDT, int QDT, int D, int B>
@@ -84,11 +109,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   // [NS stages][keys of tiles A, B][values of tiles A, B (dim-major)][fp8 scales]
   uint8_t* kt = reinterpret_cast<uint8_t*>(smem);
 
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, n = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  // Work-group order (the hardware starts work-groups in index order): sequences longest first,
+  // each one's row tiles from the last (whose queries attend the most tokens) to the first, kv
+  // heads innermost. The longest work-groups start first and short ones fill the tail; with 8 kv
+  // heads, the tiles of one (sequence, kv head) all land on the same XCD and share its L2.
+  const int wg = blockIdx.x;
+  const int g = wg % Hkv;
+  const int tile = a.num_tiles - 1 - (wg / Hkv) % a.num_tiles;
+  const int s = seq_by_length_rank(a.lens, a.num_seqs, wg / Hkv / a.num_tiles, lane, a.max_blocks * B);
 
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
@@ -466,9 +498,14 @@ static hipError_t launch_prefill_dnb(const PrefillArgs& a, int max_query_len, hi
   const int G = a.num_heads / a.num_kv_heads;
   const long long rows = static_cast<long long>(max_query_len) * G;
   constexpr int R = prefill_rows<CDT, D>();
-  const dim3 grid(static_cast<unsigned>((rows + R - 1) / R), a.num_kv_heads, a.num_seqs);
+  PrefillArgs args = a;
+  const long long tiles = (rows + R - 1) / R;
+  const long long wgs = tiles * a.num_kv_heads * a.num_seqs;  // one-dimensional grid
+  if (tiles > INT_MAX || wgs > INT_MAX) return hipErrorInvalidValue;
+  args.num_tiles = static_cast<int>(tiles);
   const size_t shm = prefill_lds_bytes<CDT, D>();
-  hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D, B>), grid, dim3(256), shm, st, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D, B>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(256), shm, st, args);
   return hipGetLastError();
 }
 

@@ -241,7 +241,7 @@ def _prefill(L, **kw):
     (dict(B=4), UNSUPPORTED), (dict(B=64), UNSUPPORTED), (dict(D=96), UNSUPPORTED),
     (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),
     (dict(qdt=F16), UNSUPPORTED), (dict(odt=F16), UNSUPPORTED), (dict(cdt=FP8, qdt=FP8), UNSUPPORTED),
-    (dict(S=70000), UNSUPPORTED), (dict(qs=None), INVALID), (dict(out=None), INVALID),
+    (dict(S=70000, mql=1 << 20), UNSUPPORTED), (dict(qs=None), INVALID), (dict(out=None), INVALID),
     (dict(cdt=FP8), INVALID), (dict(cdt=FP8, ks=FAKE), INVALID),
     (dict(T=0, out=None, q=None, kc=None, vc=None, tab=None, lens=None, qs=None, mql=0), OK),
 ])
