@@ -179,6 +179,7 @@ def measure_prefill(args, lib, torch):
         lib.pa_write_kv(d.k_new, d.v_new, d.k_cache, d.v_cache, d.slots)
         lib.pa_prefill(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, qs, w.scale, 512)
 
+    calibration_copy(args, torch)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -213,7 +214,9 @@ def measure_prefill(args, lib, torch):
                        "write_kv": round(1e3 * w_ms / max(w_n, 1), 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_mfma",
+                     "traffic": measured_traffic("prefill_mfma", "prefill-16x512-gqa-bf16",
+                                                 "prefill_hbm_traffic.txt"),
+                     "kernel": "prefill_mfma",
                      "bytes_gbs": round(w.prefill_bytes() / (k_ms * 1e-3) / 1e9, 1)},
     }
     print(json.dumps(line), flush=True)
@@ -331,23 +334,40 @@ def read_ceiling(lib, tile_bytes: int, total_bytes: int = 4 << 30, reps: int = 5
     return res
 
 
+def calibration_copy(args, torch):
+    """A plain device-to-device copy of --calibrate-copy-mib MiB: what the HBM counters read for it
+    scales their values for the kernels to bytes."""
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+
+
 def kernel_source_hash(kernel: str) -> str:
     """First 16 hex digits of sha256 over the sources the attention kernel is built from."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_318_amd", "csrc")
     h = hashlib.sha256()
-    files = ["pa_device.h", "pa_sched.h", "kv_write.h"]
-    files += ["decode_valu.hip"] if kernel == "decode_valu" else ["mfma_common.h", "decode_mfma.hip"]
+    if kernel == "prefill_mfma":
+        files = ["pa_device.h", "mfma_common.h", "prefill_mfma.hip"]
+    else:
+        files = ["pa_device.h", "pa_sched.h", "kv_write.h"]
+        files += ["decode_valu.hip"] if kernel == "decode_valu" else ["mfma_common.h", "decode_mfma.hip"]
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch (fetch + write) from the committed counter summary, or None when it has
-    no entry for this kernel and workload or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
+def measured_traffic(kernel: str, workload: str, summary: str = "decode_hbm_traffic.txt"):
+    """HBM bytes per launch (fetch + write) from a committed counter summary under profiles/, or
+    None when it has no entry for this kernel and workload or the kernel sources changed since it
+    was taken."""
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     src = kernel_source_hash(kernel)
@@ -434,14 +454,7 @@ def main():
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
                     variant=args.variant, workspace=ws, flags=flags, fused=args.fused)
 
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 20)
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+    calibration_copy(args, torch)
 
     for i in range(args.warmup):
         step(i)
