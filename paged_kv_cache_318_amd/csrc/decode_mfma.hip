@@ -48,14 +48,14 @@ constexpr int kFp8BlocksPerIter = 2;
 constexpr int mfma_blocks_per_iter(int elem_bytes) { return elem_bytes == 2 ? 2 : kFp8BlocksPerIter; }
 
 // Bytes of dynamic LDS: the staged key tiles of one iteration per wave (reused by the merge of
-// the four waves at the end of a segment) plus, for the balanced split, the batch's lengths and
-// block prefix sums.
+// the four waves at the end of a segment) plus, for the balanced split and the ordered fixed
+// partitions, the batch's lengths and prefix sums.
 template <int CDT, int D>
-constexpr size_t mfma_lds_bytes(int G, int S, bool balanced) {
+constexpr size_t mfma_lds_bytes(int G, int S, bool sched_lds) {
   const size_t stage =
       size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes;
   const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
-  const size_t sched = balanced ? (2 * static_cast<size_t>(S) + 1) * sizeof(int) : 0;
+  const size_t sched = sched_lds ? static_cast<size_t>(ordered_lds_ints(S)) * sizeof(int) : 0;
   return (stage > merge ? stage : merge) + sched;
 }
 
@@ -423,7 +423,9 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   lds_barrier();  // the LDS is free for the next segment
 }
 
-// Fixed partitions: grid (kv head, sequence, partition); one segment per work-group.
+// Fixed partitions: one segment per work-group. Grid (kv head, sequence, partition), or with
+// a.ordered a 1-D grid of (item, kv head), kv head fastest, over the ordered work list (longest
+// work first; see pa_sched.h).
 // Launch bounds ask for 3 wave64s per SIMD (at most 168 VGPRs + AGPRs per lane): 2 leaves too
 // few tiles in flight per CU, 4 forces spills.
 // NT: non-temporal K/V loads (streaming; the default) or cached ones (blocks shared between
@@ -431,10 +433,24 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
-  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int Hq = a.num_heads, G = Hq / a.num_kv_heads;
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  int g, s, p, L;
+  if (a.ordered) {
+    int* lds = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) +
+                                      mfma_lds_bytes<CDT, D>(G, 0, false));
+    g = static_cast<int>(blockIdx.x % a.num_kv_heads);
+    const int2 it = ordered_item(a, B, blockIdx.x / a.num_kv_heads, lds);
+    if (it.x < 0) return;
+    s = __builtin_amdgcn_readfirstlane(it.x);
+    p = __builtin_amdgcn_readfirstlane(it.y);
+    L = __builtin_amdgcn_readfirstlane(lds[s]);
+  } else {
+    g = blockIdx.x;
+    s = blockIdx.y;
+    p = blockIdx.z;
+    L = a.lens[s];
+    L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  }
   const int nblk = (L + B - 1) / B;
   const int b0 = p * a.part_blocks;
   if (b0 >= nblk) {
@@ -540,9 +556,11 @@ static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
     if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
     else hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
   } else {
-    const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
+    const dim3 grid = a.ordered ? dim3(a.num_kv_heads * a.num_seqs * a.max_parts)
+                                : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
+    const size_t shm_f = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.ordered != 0);
+    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm_f, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm_f, st, a);
   }
   return hipGetLastError();
 }

@@ -21,6 +21,10 @@ namespace {
 // group per work-group: fewer, heavier work-groups, each paying a few microseconds to fetch its
 // length, table entries and first tiles) is best at 1024 when there are many (sequence, kv head)
 // units to spread over the CUs, and at 2048 when there are few (long sequences, split more).
+// Over the ordered work list (longest work first, pa_sched.h) the MFMA kernel is best at 1024
+// for 256..1023 units and at 2048 from 1024 units up (log-normal lengths, median 1024: 32, 64 and
+// 128 sequences of 8 kv heads took 45.8, 76.3 and 145.7 us, against 48.1, 81.5 and 150.1 us for
+// the partition-major grid at its best length, 1024).
 // With few units the MFMA kernel instead takes the balanced split (every work-group of one
 // resident grid reads the same number of tiles): on 16 sequences of 16K..32K tokens it cut the
 // kernel from 157 to 147 us, while on 128 sequences of 64..8192 tokens (1024 units) fixed 1024-
@@ -32,6 +36,8 @@ constexpr int kDefaultPartitionValu = 512;
 constexpr int kDefaultPartitionMfma = 1024;
 constexpr int kDefaultPartitionMfmaFewUnits = 2048;
 constexpr int kFewUnits = 256;
+constexpr int kManyUnitsOrdered = 1024;
+constexpr int kDefaultPartitionMfmaOrderedMany = 2048;
 constexpr int kMaxGridYZ = 65535;
 
 bool dtype_ok(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
@@ -111,11 +117,13 @@ struct Plan {
   int max_parts;
 };
 Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens,
-                     bool mfma = false, long long units = 0) {
+                     bool mfma = false, long long units = 0, bool ordered = false) {
   int pt = partition_tokens;
   if (pt <= 0) {
     pt = !mfma ? kDefaultPartitionValu
-               : (units >= kFewUnits ? kDefaultPartitionMfma : kDefaultPartitionMfmaFewUnits);
+               : (units < kFewUnits ? kDefaultPartitionMfmaFewUnits
+                                    : (ordered && units >= kManyUnitsOrdered ? kDefaultPartitionMfmaOrderedMany
+                                                                             : kDefaultPartitionMfma));
   }
   int pb = pt / block_size;
   if (pb < 1) pb = 1;
@@ -374,13 +382,17 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   } else {
     use_mfma = mfma_ok && G >= 2;
   }
-  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma,
-                                  static_cast<long long>(num_seqs) * num_kv_heads);
-  if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
-  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  const long long units = static_cast<long long>(num_seqs) * num_kv_heads;
   // Default plan for the MFMA kernel on few units: the balanced split over one resident grid.
   const bool balanced =
       partition_tokens == 0 && use_mfma && balanced_eligible(num_seqs, num_kv_heads, max_blocks_per_seq);
+  // Fixed MFMA partitions run over the ordered work list (longest work first) when the batch's
+  // lengths fit the ordering's LDS.
+  const bool order_ok = use_mfma && !balanced && num_seqs <= pa::kOrderedMaxSeqs;
+  const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma, units,
+                                  order_ok);
+  if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
   int nw = 0;
   if (balanced) {
     const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs,
@@ -425,6 +437,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.heads_per_unit = gu;
   a.balanced = balanced ? 1 : 0;
   a.nw = nw;
+  // (the ordered list's 1-D grid must also fit)
+  a.ordered = (order_ok && units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_slots = k_new != nullptr ? slot_mapping : nullptr;

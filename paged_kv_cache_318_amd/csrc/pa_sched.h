@@ -80,6 +80,119 @@ __device__ inline void scan_batch(const DecodeArgs& a, int B, int* lens_lds, int
   __syncthreads();
 }
 
+// Whole work-group: exclusive prefix of `local` over the threads in thread order; *total gets the
+// sum. Needs blockDim.x a multiple of 64 and at most 1024.
+__device__ inline int block_exclusive_scan(int local, int* total) {
+  __shared__ int wave_tot[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  int v = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    before += w < wave ? wave_tot[w] : 0;
+    all += wave_tot[w];
+  }
+  __syncthreads();  // wave_tot may be reused by the next scan
+  *total = all;
+  return before + v - local;
+}
+
+// ---- ordered fixed partitions -------------------------------------------------------------------
+//
+// With fixed partitions every (sequence, partition) pair is one work-group per unit. Launched in
+// partition-major order, the grid ends with the full partitions of the longest sequences: on a
+// long-tailed length mix (128 sequences, log-normal median 1024, up to 8192, 1024-token partitions)
+// the last of them started some 120 us into a 150 us kernel and ran on an emptying GPU for their
+// last 20-30 us, and two thirds of the launched work-groups found an empty partition. The ordered
+// grid lists the work longest first: every full partition (sequence-major), then each sequence's
+// last, partial partition bucketed by its length, longest bucket first (sequence order within a
+// bucket); a sequence with no tokens has one empty item, last, that writes its zero output. Grid
+// items past the list end at once. Which work-group computes an item changes nothing in its
+// result.
+
+constexpr int kOrderBuckets = 16;
+constexpr int kOrderedMaxSeqs = 1024;
+
+// LDS ints the ordering needs for S sequences.
+__host__ __device__ constexpr int ordered_lds_ints(int S) { return 2 * S + 1 + kOrderBuckets + 1; }
+
+// Whole work-group (uniform k): the (sequence, partition) of item k of the ordered list, or
+// sequence -1 past its end. lds: ordered_lds_ints(S) ints; on return lds[s] is the clamped
+// context length of sequence s.
+__device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int* lds) {
+  const int S = a.num_seqs, nt = blockDim.x, tid = threadIdx.x, pb = a.part_blocks;
+  int* lens_l = lds;                // [S]
+  int* pref = lds + S;              // [S + 1] full partitions before sequence s
+  int* bcnt = pref + S + 1;         // [kOrderBuckets + 1] last partitions per bucket
+  __shared__ int found;
+  const int per = (S + nt - 1) / nt;
+  const int beg = min(S, tid * per), end = min(S, beg + per);
+  const int cap = a.max_blocks * B;
+  if (tid <= kOrderBuckets) bcnt[tid] = 0;
+  __syncthreads();
+  // bucket of a sequence's last item: blocks in its partial partition, longest first; a sequence
+  // with no tokens goes last; -1: no partial partition
+  auto bucket = [&](int nblk) {
+    const int rem = nblk % pb;
+    return nblk == 0 ? kOrderBuckets - 1 : (rem == 0 ? -1 : (pb - rem) * kOrderBuckets / pb);
+  };
+  int nfull = 0;
+  for (int s = beg; s < end; ++s) {
+    int L = a.lens[s];
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+    lens_l[s] = L;
+    const int nblk = (L + B - 1) / B;
+    nfull += nblk / pb;
+    const int b = bucket(nblk);
+    if (b >= 0) atomicAdd(&bcnt[b], 1);
+  }
+  int F = 0;
+  int excl = block_exclusive_scan(nfull, &F);
+  for (int s = beg; s < end; ++s) {
+    pref[s] = excl;
+    excl += ((lens_l[s] + B - 1) / B) / pb;
+  }
+  if (tid == 0) pref[S] = F;
+  __syncthreads();
+  if (k < F) {  // the largest s with pref[s] <= k (its interval [pref[s], pref[s+1]) holds k)
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pref[mid] <= k) lo = mid;
+      else hi = mid;
+    }
+    return make_int2(lo, static_cast<int>(k - pref[lo]));
+  }
+  long long r = k - F;
+  int b = 0;
+  for (; b < kOrderBuckets; ++b) {
+    if (r < bcnt[b]) break;
+    r -= bcnt[b];
+  }
+  if (b == kOrderBuckets) return make_int2(-1, 0);
+  // the r-th sequence (in sequence order) whose last item lies in bucket b
+  int mine = 0;
+  for (int s = beg; s < end; ++s) mine += bucket((lens_l[s] + B - 1) / B) == b ? 1 : 0;
+  int cnt = 0;
+  int before = block_exclusive_scan(mine, &cnt);
+  if (r >= before && r < before + mine) {
+    for (int s = beg; s < end; ++s) {
+      if (bucket((lens_l[s] + B - 1) / B) != b) continue;
+      if (before == r) found = s;
+      ++before;
+    }
+  }
+  __syncthreads();
+  const int s = found;
+  return make_int2(s, ((lens_l[s] + B - 1) / B) / pb);
+}
+
 // The sequence holding tile t (t < pref[S] * hu): the largest s with pref[s] * hu <= t, which is
 // never an empty sequence.
 __device__ __forceinline__ int find_seq(const int* pref, int S, long long hu, long long t) {

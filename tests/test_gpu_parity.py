@@ -237,6 +237,77 @@ def test_balanced_split_cuts_units(lens, cdt, B):
     assert np.array_equal(got, run_gpu(w, out_dt="f32", variant=2))
 
 
+@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
+def test_balanced_split_reuses_one_workspace(cdt):
+    """One workspace serves the balanced split of a long batch, of a short one and of the long one
+    again: each result the same bits as with a workspace of its own (nothing a call leaves in the
+    workspace reaches the next call's output)."""
+    long_w = make_workload([9000, 1, 4000, 2500], num_heads=8, num_kv_heads=2, head_dim=128,
+                           dtype=cdt, q_dtype="bf16", seed=71)
+    short_w = make_workload([300, 40], num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt,
+                            q_dtype="bf16", seed=72)
+    for w in (long_w, short_w):
+        _check_inputs(w)
+    dl, dsh = upload(long_w), upload(short_w)
+    ws = workspace_for(dl.q, dl.k_cache, dl.tables, 16)
+    assert ws.numel() >= workspace_for(dsh.q, dsh.k_cache, dsh.tables, 16).numel()
+
+    def once(w, d, workspace):  # the slot write (the same bits every time), then pa_decode
+        out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch.float32, device="cuda")
+        decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
+                    d.cow, w.scale, d.k_scale, d.v_scale, variant=2, workspace=workspace,
+                    fused=False)
+        torch.cuda.synchronize()
+        return to_numpy_f64(out)
+
+    fresh_long = once(long_w, dl, workspace_for(dl.q, dl.k_cache, dl.tables, 16))
+    fresh_short = once(short_w, dsh, workspace_for(dsh.q, dsh.k_cache, dsh.tables, 16))
+    for w, d, fresh in ((long_w, dl, fresh_long), (short_w, dsh, fresh_short),
+                        (long_w, dl, fresh_long)):
+        got = once(w, d, ws)
+        assert np.array_equal(got, fresh)
+    assert_close(fresh_long, run_oracle(long_w), cdt, "f32", f"balanced, reused workspace, {cdt}")
+
+
+@pytest.mark.parametrize("cdt,B", [("bf16", 16), ("fp8", 16), ("bf16", 8), ("fp8", 32)])
+def test_ordered_fixed_partitions(cdt, B):
+    """Fixed MFMA partitions run over the ordered work list (full partitions first, then each
+    sequence's last partition by length, empty sequences last): empty sequences, lengths that
+    fill whole partitions, one- and two-token remainders and long sequences, against the oracle."""
+    lens = [0, 256, 512, 257, 300, 1, 16, 17, 255, 768, 0, 1000, 4096, 4095, 2, 511, 513, 129]
+    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype="bf16",
+                      block_size=B, seed=81)
+    ref = run_oracle(w)
+    got = run_gpu(w, out_dt="f32", part=256, variant=2, fused=False)
+    assert_close(got, ref, cdt, "f32", f"ordered partitions {cdt} B={B}")
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=256, variant=2, fused=False))
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=256, variant=2, fused=True))
+
+
+def test_ordered_grid_matches_the_plain_grid_bit_for_bit():
+    """The ordered grid serves batches of up to 1024 sequences; a batch of 1025 takes the plain
+    (kv head, sequence, partition) grid. Both compute every (sequence, partition) item with the
+    same code, so decoding the first 1024 sequences of a 1025-sequence batch gives the same bits
+    as decoding the whole batch."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(0, 700, size=1025)
+    lens[::97] = 0
+    w = make_workload(lens.tolist(), num_heads=8, num_kv_heads=2, head_dim=64, dtype="bf16", seed=92)
+    _check_inputs(w)
+    d = upload(w)
+    out = torch.empty(1025, 8, 64, dtype=torch.float32, device="cuda")
+    decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
+                w.scale, d.k_scale, d.v_scale, partition_tokens=128, variant=2,
+                workspace=workspace_for(d.q, d.k_cache, d.tables, 16, 128), fused=False)
+    out2 = torch.empty(1024, 8, 64, dtype=torch.float32, device="cuda")
+    lib.pa_decode(out2, d.q[:1024], d.k_cache, d.v_cache, d.tables[:1024], d.lens[:1024], w.scale,
+                  d.k_scale, d.v_scale, partition_tokens=128, variant=2,
+                  workspace=workspace_for(d.q[:1024], d.k_cache, d.tables[:1024], 16, 128))
+    torch.cuda.synchronize()
+    assert torch.equal(out[:1024], out2)
+    assert_close(to_numpy_f64(out), run_oracle(w), "bf16", "f32", "1025 sequences, plain grid")
+
+
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,D,B,variant", COMBOS)
 @pytest.mark.parametrize("part", [0, 256])
 def test_separate_write_and_decode_parity(cdt, qdt, hq, hkv, D, B, variant, part):
