@@ -465,8 +465,9 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
                                 (static_cast<size_t>(s) * a.num_kv_heads + g) * a.max_parts + p, G, -1);
 }
 
-// Balanced split: work-group i of a.nw takes tiles [i*W/nw, (i+1)*W/nw) of the flattened
-// (sequence, kv head, block) list and walks them unit by unit.
+// Balanced split: work-group i of a.nw takes share i (tiles [share_lo(i), share_lo(i+1)) of the
+// flattened (sequence, kv head, block) list, weighted by its place on its CU) and walks it unit by
+// unit.
 template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs
     for (int k = threadIdx.x; k <= a.num_seqs; k += blockDim.x) a.ws_pref[k] = pref[k];
   const int nw = balanced_groups(W, a.nw);
   if (i >= nw) return;
-  const long long lo = share_lo(W, nw, i), hi = share_lo(W, nw, i + 1);
+  const long long lo = share_lo(W, nw, a.nw_cls, i), hi = share_lo(W, nw, a.nw_cls, i + 1);
   long long t = lo;
   while (t < hi) {
     const int s = find_seq(pref, a.num_seqs, hu, t);

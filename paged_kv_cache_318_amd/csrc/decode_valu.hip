@@ -278,11 +278,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
     const long long W = static_cast<long long>(a.ws_pref[a.num_seqs]) * hu;
     const int nw = balanced_groups(W, a.nw);
     const long long ustart = static_cast<long long>(p0) * hu + static_cast<long long>(x) * nb;
-    i0 = share_owner(W, nw, ustart);
-    const int i1 = share_owner(W, nw, ustart + nb - 1);
+    i0 = share_owner(W, nw, a.nw_cls, ustart);
+    const int i1 = share_owner(W, nw, a.nw_cls, ustart + nb - 1);
     if (i0 == i1) return;  // one work-group took the whole unit and wrote its output
     count = i1 - i0 + 1;   // every share is non-empty, so each of these holds a partial result
-    i0_first = share_lo(W, nw, i0) == ustart;
+    i0_first = share_lo(W, nw, a.nw_cls, i0) == ustart;
   } else {
     int L = a.lens[s];
     L = L < 0 ? 0 : (L > a.max_blocks * block_size ? a.max_blocks * block_size : L);

@@ -393,13 +393,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                                   order_ok);
   if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
-  int nw = 0;
+  int nw = 0, nw_cls = 0;
   if (balanced) {
     const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs,
                                               stream_kv);
     const int cus = cu_count();
     nw = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
     nw = nw > pa::kMaxBalancedGroups ? pa::kMaxBalancedGroups : nw;
+    // three resident work-groups per CU: shares weighted by their order of arrival on the CU
+    if (cus > 0 && per_cu == 3 && nw == 3 * cus) nw_cls = cus;
   }
   const int gu = use_mfma ? G : 1;
   const size_t slots = balanced ? 2 * static_cast<size_t>(nw)
@@ -437,6 +439,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.heads_per_unit = gu;
   a.balanced = balanced ? 1 : 0;
   a.nw = nw;
+  a.nw_cls = nw_cls;
   // (the ordered list's 1-D grid must also fit)
   a.ordered = (order_ok && units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
   a.k_new = k_new;

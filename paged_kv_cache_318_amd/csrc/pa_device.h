@@ -221,6 +221,7 @@ struct DecodeArgs {
   int heads_per_unit;  // query heads one work-group accumulates: 1 (VALU) or Hq / Hkv (MFMA)
   int balanced;    // 1: balanced split over nw work-groups; 0: fixed partitions
   int nw;
+  int nw_cls;      // balanced split: CUs of a grid of three work-groups per CU (weighted shares), or 0
   int ordered;     // fixed partitions, MFMA kernel: 1-D grid over the ordered work list
   float zscale;    // softmax scale * log2(e)
   // pa_decode_append: the batch's new tokens ([S][Hkv][D], the cache dtype, or the query dtype for

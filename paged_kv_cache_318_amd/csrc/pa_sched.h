@@ -31,14 +31,46 @@ __device__ __forceinline__ int balanced_groups(long long W, int nw) {
   return n < 1 ? 1 : (n > nw ? nw : static_cast<int>(n));
 }
 
-// Work-group i's share starts at tile i*W/nw.
-__device__ __forceinline__ long long share_lo(long long W, int nw, int i) {
-  return (W * i) / nw;
+// Shares weighted by the work-group's place on its CU. The resident grid is dispatched one
+// work-group per CU at a time, so with cls CUs and three work-groups per CU, work-group i is the
+// (i / cls)-th to arrive on its CU. The three do not progress at the same rate: the CU favours its
+// older waves, and with equal shares the first, second and third to arrive finished after ~94, ~104
+// and ~134 us (16 fp8 sequences of 16K..32K tokens), the last third running alone on its CU at about
+// two thirds of the CU's rate. Shares in the proportion 28 : 20 : 12 bring the three close to
+// finishing together: that batch's kernel took 135.2 us, against 149.1 with equal shares, 144.3 at
+// 24 : 20 : 16, 138.4 at 26 : 20 : 14 and 140.5 at 30 : 20 : 10. The shares depend only on the batch
+// and the CU count, so results stay deterministic.
+constexpr int kSlotWeight0 = 28, kSlotWeight1 = 20, kSlotWeight2 = 12;
+constexpr int kSlotWeightSum = kSlotWeight0 + kSlotWeight1 + kSlotWeight2;
+
+// Weight units before work-group i (weighted grid of 3 * cls work-groups).
+__device__ __forceinline__ long long slot_weight_before(int cls, int i) {
+  if (i < cls) return static_cast<long long>(i) * kSlotWeight0;
+  if (i < 2 * cls) return static_cast<long long>(cls) * kSlotWeight0 + static_cast<long long>(i - cls) * kSlotWeight1;
+  return static_cast<long long>(cls) * (kSlotWeight0 + kSlotWeight1) +
+         static_cast<long long>(i - 2 * cls) * kSlotWeight2;  // (i = 3 * cls: the total)
+}
+
+// Work-group i's share starts at tile i*W/nw, or at its weighted place when cls > 0 and the grid is
+// the weighted one (nw == 3 * cls).
+__device__ __forceinline__ long long share_lo(long long W, int nw, int cls, int i) {
+  if (cls <= 0 || nw != 3 * cls) return (W * i) / nw;
+  return (W * slot_weight_before(cls, i)) / (static_cast<long long>(cls) * kSlotWeightSum);
 }
 
 // The work-group whose share holds tile t: the largest i with share_lo(i) <= t.
-__device__ __forceinline__ int share_owner(long long W, int nw, long long t) {
-  return static_cast<int>(((t + 1) * nw - 1) / W);
+__device__ __forceinline__ int share_owner(long long W, int nw, int cls, long long t) {
+  if (cls <= 0 || nw != 3 * cls) return static_cast<int>(((t + 1) * nw - 1) / W);
+  // share_lo(i) <= t  <=>  slot_weight_before(i) <= X, X = floor(((t + 1) * T - 1) / W)
+  const long long T = static_cast<long long>(cls) * kSlotWeightSum;
+  const long long X = ((t + 1) * T - 1) / W;
+  const long long c1 = static_cast<long long>(cls) * kSlotWeight0;
+  const long long c2 = c1 + static_cast<long long>(cls) * kSlotWeight1;
+  int i;
+  if (X >= c2) i = 2 * cls + static_cast<int>((X - c2) / kSlotWeight2);
+  else if (X >= c1) i = cls + static_cast<int>((X - c1) / kSlotWeight1);
+  else i = static_cast<int>(X / kSlotWeight0);
+  return i < nw - 1 ? i : nw - 1;
 }
 
 // Whole work-group: lens_lds[s] = clamped context length of sequence s, pref[s] = blocks of the

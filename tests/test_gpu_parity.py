@@ -238,6 +238,20 @@ def test_balanced_split_cuts_units(lens, cdt, B):
 
 
 @pytest.mark.parametrize("cdt", ["bf16", "fp8"])
+def test_balanced_split_weighted_shares(cdt):
+    """A batch long enough for the whole resident grid (three work-groups per CU) gets shares
+    weighted by each work-group's order of arrival on its CU: parity with the oracle, with explicit
+    partitions within tolerance, and the same bits on a second call."""
+    w = make_workload([30000, 20000, 1, 9000], num_heads=16, num_kv_heads=4, head_dim=128,
+                      dtype=cdt, q_dtype="bf16", seed=61)
+    ref = run_oracle(w)
+    got = run_gpu(w, out_dt="f32", variant=2, fused=False)
+    assert_close(got, ref, cdt, "f32", f"weighted balanced split {cdt}")
+    assert np.max(np.abs(got - run_gpu(w, out_dt="f32", part=2048, variant=2, fused=False))) <= TOL[cdt]
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", variant=2, fused=True))
+
+
+@pytest.mark.parametrize("cdt", ["bf16", "fp8"])
 def test_balanced_split_reuses_one_workspace(cdt):
     """One workspace serves the balanced split of a long batch, of a short one and of the long one
     again: each result the same bits as with a workspace of its own (nothing a call leaves in the
