@@ -25,12 +25,12 @@ namespace {
 // for 256..1023 units and at 2048 from 1024 units up (log-normal lengths, median 1024: 32, 64 and
 // 128 sequences of 8 kv heads took 45.8, 76.3 and 145.7 us, against 48.1, 81.5 and 150.1 us for
 // the partition-major grid at its best length, 1024).
-// With few units the MFMA kernel instead takes the balanced split (every work-group of one
-// resident grid reads the same number of tiles): on 16 sequences of 16K..32K tokens it cut the
-// kernel from 157 to 147 us, while on 128 sequences of 64..8192 tokens (1024 units) fixed 1024-
-// token partitions stay faster (151 us against 155..165 us for grids of 1x..4x the resident
-// work-groups), since there a work-group walks several short units, each starting with a latency
-// bubble the hardware's own dispatch of many small work-groups hides better.
+// With few units the MFMA kernel instead takes the balanced split (one resident grid, each
+// work-group a share of the tiles weighted by its order of arrival on its CU): on 16 sequences of
+// 16K..32K tokens it takes 135 us, against 141 us for ordered 2048-token partitions, while on 128
+// sequences of 64..8192 tokens (1024 units) the ordered partitions stay faster (146 us against
+// 159 us), since there a work-group walks several short units, each starting with a table fetch
+// and a first load round trip with nothing in flight.
 // Workspaces are sized for the largest of these plans, so they fit every choice.
 constexpr int kDefaultPartitionValu = 512;
 constexpr int kDefaultPartitionMfma = 1024;

@@ -1,0 +1,117 @@
+"""Host model of the decode kernels' work-split arithmetic (csrc/pa_sched.h), restated in Python.
+
+The kernels' results are checked on the GPU against the oracle; these tests check the integer
+arithmetic that decides which work-group reads which tiles, on many shapes at no GPU cost:
+
+* balanced split -- shares (equal, or weighted 28 : 20 : 12 by a work-group's order of arrival on
+  its CU when the grid holds three work-groups per CU) cover the flattened tile list exactly once,
+  none is empty, and share_owner -- which the merge kernel uses to find the partial results of a
+  unit -- names the share that holds every tile;
+* ordered fixed partitions -- the ordered list holds every (sequence, partition) item exactly once
+  plus one item per empty sequence, full partitions first, then last partitions longest class
+  first, and the grid covers it.
+"""
+
+import random
+
+import pytest
+
+K_MIN_SHARE_TILES = 16
+W0, W1, W2 = 28, 20, 12
+BUCKETS = 16
+
+
+def balanced_groups(W, nw):
+    n = W // K_MIN_SHARE_TILES
+    return 1 if n < 1 else min(n, nw)
+
+
+def weight_before(cls, i):
+    if i < cls:
+        return i * W0
+    if i < 2 * cls:
+        return cls * W0 + (i - cls) * W1
+    return cls * (W0 + W1) + (i - 2 * cls) * W2
+
+
+def share_lo(W, nw, cls, i):
+    if cls <= 0 or nw != 3 * cls:
+        return (W * i) // nw
+    return (W * weight_before(cls, i)) // (cls * (W0 + W1 + W2))
+
+
+def share_owner(W, nw, cls, t):
+    if cls <= 0 or nw != 3 * cls:
+        return ((t + 1) * nw - 1) // W
+    T = cls * (W0 + W1 + W2)
+    X = ((t + 1) * T - 1) // W
+    c1 = cls * W0
+    c2 = c1 + cls * W1
+    if X >= c2:
+        i = 2 * cls + (X - c2) // W2
+    elif X >= c1:
+        i = cls + (X - c1) // W1
+    else:
+        i = X // W0
+    return min(i, nw - 1)
+
+
+@pytest.mark.parametrize("cls", [0, 1, 2, 5, 64, 256, 304])
+def test_balanced_shares_cover_the_tiles_once(cls):
+    rng = random.Random(cls)
+    for _ in range(40):
+        grid = 3 * cls if cls else rng.choice([1, 7, 768, 1024])
+        W = rng.randint(1, 16 * grid * 50)
+        nw = balanced_groups(W, grid)
+        c = cls  # the CU count; the weights apply only while nw == 3 * cls
+        bounds = [share_lo(W, nw, c, i) for i in range(nw + 1)]
+        assert bounds[0] == 0 and bounds[-1] == W
+        sizes = [b - a for a, b in zip(bounds, bounds[1:])]
+        assert min(sizes) >= 1
+        if nw == 3 * cls and cls:
+            # the weighted shares follow the weights (within one tile)
+            unit = W / (cls * (W0 + W1 + W2))
+            for i, sz in enumerate(sizes):
+                w = W0 if i < cls else (W1 if i < 2 * cls else W2)
+                assert abs(sz - w * unit) <= 1
+        for t in rng.sample(range(W), min(W, 3000)) + [0, W - 1]:
+            i = share_owner(W, nw, c, t)
+            assert bounds[i] <= t < bounds[i + 1]
+
+
+def ordered_items(lens, B, pb):
+    """The ordered list of (sequence, partition) items, as ordered_item enumerates it."""
+    nblk = [(L + B - 1) // B for L in lens]
+
+    def bucket(n):
+        rem = n % pb
+        return BUCKETS - 1 if n == 0 else (-1 if rem == 0 else (pb - rem) * BUCKETS // pb)
+
+    full = [(s, p) for s, n in enumerate(nblk) for p in range(n // pb)]
+    last = []
+    for b in range(BUCKETS):
+        last += [(s, n // pb) for s, n in enumerate(nblk) if bucket(n) == b]
+    return full + last
+
+
+@pytest.mark.parametrize("pb", [1, 2, 3, 16, 64, 128])
+def test_ordered_list_holds_every_item_once(pb):
+    rng = random.Random(pb)
+    B = 16
+    for _ in range(30):
+        S = rng.randint(1, 300)
+        lens = [rng.choice([0, rng.randint(1, 40 * B * pb)]) for _ in range(S)]
+        items = ordered_items(lens, B, pb)
+        nblk = [(L + B - 1) // B for L in lens]
+        expect = {(s, p) for s, n in enumerate(nblk) for p in range((n + pb - 1) // pb)}
+        expect |= {(s, 0) for s, n in enumerate(nblk) if n == 0}
+        assert len(items) == len(expect) and set(items) == expect
+        max_parts = max(1, (max(nblk) + pb - 1) // pb)
+        assert len(items) <= S * max_parts  # the launched grid covers the list
+        # full partitions first, then the last partitions by non-increasing length, empty ones last
+        sizes = [min(pb, n - p * pb) for (s, p) in items for n in [nblk[s]]]
+        nf = sum(n // pb for n in nblk)
+        assert all(x == pb for x in sizes[:nf])
+        tail = sizes[nf:]
+        cls = [BUCKETS - 1 if x == 0 else (pb - x) * BUCKETS // pb for x in tail]
+        assert cls == sorted(cls)
