@@ -35,20 +35,36 @@ constexpr int kValuBlocksPerIter = 2;
 
 // NT: read K/V tiles non-temporally (streaming; the default) or through the caches (when blocks
 // are shared between sequences of the batch and a tile fetched for one is reused by another).
+// Grid (query head, sequence, partition), or with a.ordered a 1-D grid of (item, query head),
+// query head fastest, over the ordered work list (longest work first; see pa_sched.h), the lengths
+// staged in dynamic LDS.
 template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int QB = Elem<QDT>::bytes;
   constexpr int DPL = D / 16;  // key dims per lane
   constexpr int TPR = B / 4;   // tokens per 16-lane row
-  const int h = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane >> 4, c = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
 
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  int h, s, p, L;
+  if (a.ordered) {
+    extern __shared__ int order_lds[];
+    h = static_cast<int>(blockIdx.x % Hq);
+    const int2 it = ordered_item(a, B, blockIdx.x / Hq, order_lds);
+    if (it.x < 0) return;
+    s = __builtin_amdgcn_readfirstlane(it.x);
+    p = __builtin_amdgcn_readfirstlane(it.y);
+    L = __builtin_amdgcn_readfirstlane(order_lds[s]);
+  } else {
+    h = blockIdx.x;
+    s = blockIdx.y;
+    p = blockIdx.z;
+    L = a.lens[s];
+    L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+  }
   const int nblk = (L + B - 1) / B;
   const int b0 = p * a.part_blocks;
   const size_t orow = (static_cast<size_t>(s) * Hq + h) * D;
@@ -355,8 +371,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
 // ---- launchers ----------------------------------------------------------------------------------
 template <int CDT, int QDT, int D, int B>
 static void launch_valu_nt(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  if (a.stream_kv) hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, false>), grid, dim3(256), 0, st, a);
+  const size_t shm = a.ordered ? static_cast<size_t>(ordered_lds_ints(a.num_seqs)) * sizeof(int) : 0;
+  if (a.stream_kv) hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+  else hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
 }
 
 template <int CDT, int QDT, int D>
@@ -378,7 +395,8 @@ static hipError_t launch_valu_d(const DecodeArgs& a, int D, int B, dim3 grid, hi
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int cdt, int qdt, int D, int B, hipStream_t st) {
-  const dim3 grid(a.num_heads, a.num_seqs, a.max_parts);
+  const dim3 grid = a.ordered ? dim3(a.num_heads * a.num_seqs * a.max_parts)
+                              : dim3(a.num_heads, a.num_seqs, a.max_parts);
   if (cdt == DT_F32 && qdt == DT_F32) return launch_valu_d<DT_F32, DT_F32>(a, D, B, grid, st);
   if (cdt == DT_F16 && qdt == DT_F16) return launch_valu_d<DT_F16, DT_F16>(a, D, B, grid, st);
   if (cdt == DT_BF16 && qdt == DT_BF16) return launch_valu_d<DT_BF16, DT_BF16>(a, D, B, grid, st);

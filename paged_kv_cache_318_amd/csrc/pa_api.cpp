@@ -17,7 +17,11 @@
 namespace {
 
 // Default partition lengths (tokens), from sweeps of 128..8192 on the decode workloads. The
-// VALU kernel (one query head per work-group) is best at 512. The MFMA kernel (a whole query
+// VALU kernel (one query head per work-group) is best at 512 on the partition-major grid, and over
+// the ordered work list at 2048 once the batch has 2048 (sequence, query head) units or more (64
+// sequences of 128..2048 tokens, 40 heads: 253.2 us with no merge launch, against 255.5 us + the
+// merge at 512 partition-major; ordered 512 took 261.1 us, its many work-groups each paying the
+// ordering's scans). The MFMA kernel (a whole query
 // group per work-group: fewer, heavier work-groups, each paying a few microseconds to fetch its
 // length, table entries and first tiles) is best at 1024 when there are many (sequence, kv head)
 // units to spread over the CUs, and at 2048 when there are few (long sequences, split more).
@@ -31,8 +35,15 @@ namespace {
 // sequences of 64..8192 tokens (1024 units) the ordered partitions stay faster (146 us against
 // 159 us), since there a work-group walks several short units, each starting with a table fetch
 // and a first load round trip with nothing in flight.
+// The ordered list is used from 1024-token partitions up, and not when sequences share blocks
+// (PA_DECODE_SHARED_BLOCKS): there the partition-major grid keeps the samples of a prompt, whose
+// shared blocks one fetch serves through the L2, running together (shared-prefix batch, 512-token
+// partitions: 99.2 us against 104.7 us ordered).
 // Workspaces are sized for the largest of these plans, so they fit every choice.
 constexpr int kDefaultPartitionValu = 512;
+constexpr int kDefaultPartitionValuOrdered = 2048;
+constexpr int kManyValuUnitsOrdered = 2048;
+constexpr int kMinOrderedPartition = 1024;
 constexpr int kDefaultPartitionMfma = 1024;
 constexpr int kDefaultPartitionMfmaFewUnits = 2048;
 constexpr int kFewUnits = 256;
@@ -116,14 +127,18 @@ struct Plan {
   int part_blocks;
   int max_parts;
 };
+// units: (sequence, kv head) units for the MFMA kernel, (sequence, query head) for the VALU kernel;
+// ordered: the batch may run over the ordered work list.
 Plan plan_partitions(int max_blocks_per_seq, int block_size, int partition_tokens,
                      bool mfma = false, long long units = 0, bool ordered = false) {
   int pt = partition_tokens;
   if (pt <= 0) {
-    pt = !mfma ? kDefaultPartitionValu
-               : (units < kFewUnits ? kDefaultPartitionMfmaFewUnits
-                                    : (ordered && units >= kManyUnitsOrdered ? kDefaultPartitionMfmaOrderedMany
-                                                                             : kDefaultPartitionMfma));
+    if (!mfma)
+      pt = ordered && units >= kManyValuUnitsOrdered ? kDefaultPartitionValuOrdered : kDefaultPartitionValu;
+    else
+      pt = units < kFewUnits ? kDefaultPartitionMfmaFewUnits
+                             : (ordered && units >= kManyUnitsOrdered ? kDefaultPartitionMfmaOrderedMany
+                                                                      : kDefaultPartitionMfma);
   }
   int pb = pt / block_size;
   if (pb < 1) pb = 1;
@@ -382,17 +397,19 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   } else {
     use_mfma = mfma_ok && G >= 2;
   }
-  const long long units = static_cast<long long>(num_seqs) * num_kv_heads;
+  const long long units = static_cast<long long>(num_seqs) * (use_mfma ? num_kv_heads : num_heads);
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
   // Default plan for the MFMA kernel on few units: the balanced split over one resident grid.
   const bool balanced =
       partition_tokens == 0 && use_mfma && balanced_eligible(num_seqs, num_kv_heads, max_blocks_per_seq);
-  // Fixed MFMA partitions run over the ordered work list (longest work first) when the batch's
-  // lengths fit the ordering's LDS.
-  const bool order_ok = use_mfma && !balanced && num_seqs <= pa::kOrderedMaxSeqs;
+  // Fixed partitions may run over the ordered work list (longest work first) when the batch's
+  // lengths fit the ordering's LDS. The partition length does not depend on the shared-blocks
+  // flag, which only selects the cache policy and the grid order: the same inputs give the same
+  // bits with or without it.
+  const bool order_ok = !balanced && num_seqs <= pa::kOrderedMaxSeqs;
   const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma, units,
                                   order_ok);
   if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
-  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
   int nw = 0, nw_cls = 0;
   if (balanced) {
     const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs,
@@ -441,7 +458,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.nw = nw;
   a.nw_cls = nw_cls;
   // (the ordered list's 1-D grid must also fit)
-  a.ordered = (order_ok && units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
+  a.ordered = (order_ok && stream_kv && static_cast<int64_t>(pl.part_blocks) * block_size >= kMinOrderedPartition &&
+               units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_slots = k_new != nullptr ? slot_mapping : nullptr;

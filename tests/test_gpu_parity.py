@@ -283,40 +283,45 @@ def test_balanced_split_reuses_one_workspace(cdt):
     assert_close(fresh_long, run_oracle(long_w), cdt, "f32", f"balanced, reused workspace, {cdt}")
 
 
-@pytest.mark.parametrize("cdt,B", [("bf16", 16), ("fp8", 16), ("bf16", 8), ("fp8", 32)])
-def test_ordered_fixed_partitions(cdt, B):
-    """Fixed MFMA partitions run over the ordered work list (full partitions first, then each
-    sequence's last partition by length, empty sequences last): empty sequences, lengths that
-    fill whole partitions, one- and two-token remainders and long sequences, against the oracle."""
-    lens = [0, 256, 512, 257, 300, 1, 16, 17, 255, 768, 0, 1000, 4096, 4095, 2, 511, 513, 129]
-    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype="bf16",
+@pytest.mark.parametrize("cdt,qdt,B,variant", [("bf16", "bf16", 16, 2), ("fp8", "bf16", 16, 2),
+                                              ("bf16", "bf16", 8, 2), ("fp8", "f16", 32, 2),
+                                              ("f16", "f16", 16, 1), ("f32", "f32", 16, 1),
+                                              ("fp8", "bf16", 32, 1)])
+def test_ordered_fixed_partitions(cdt, qdt, B, variant):
+    """Fixed partitions of 1024 tokens or more run over the ordered work list (full partitions
+    first, then each sequence's last partition by length, empty sequences last), in both decode
+    kernels: empty sequences, lengths that fill whole partitions, one- and two-token remainders
+    and long sequences, against the oracle; fused and separate steps give the same bits."""
+    lens = [0, 1024, 2048, 1025, 1100, 1, 16, 17, 1023, 3072, 0, 4000, 8192, 8191, 2, 2047, 2049, 129]
+    w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype=cdt, q_dtype=qdt,
                       block_size=B, seed=81)
     ref = run_oracle(w)
-    got = run_gpu(w, out_dt="f32", part=256, variant=2, fused=False)
-    assert_close(got, ref, cdt, "f32", f"ordered partitions {cdt} B={B}")
-    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=256, variant=2, fused=False))
-    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=256, variant=2, fused=True))
+    got = run_gpu(w, out_dt="f32", part=1024, variant=variant, fused=False)
+    assert_close(got, ref, cdt, "f32", f"ordered partitions {cdt} B={B} v={variant}")
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=1024, variant=variant, fused=False))
+    assert np.array_equal(got, run_gpu(w, out_dt="f32", part=1024, variant=variant, fused=True))
 
 
-def test_ordered_grid_matches_the_plain_grid_bit_for_bit():
+@pytest.mark.parametrize("variant", [1, 2])
+def test_ordered_grid_matches_the_plain_grid_bit_for_bit(variant):
     """The ordered grid serves batches of up to 1024 sequences; a batch of 1025 takes the plain
-    (kv head, sequence, partition) grid. Both compute every (sequence, partition) item with the
-    same code, so decoding the first 1024 sequences of a 1025-sequence batch gives the same bits
-    as decoding the whole batch."""
+    (head, sequence, partition) grid. Both compute every (sequence, partition) item with the same
+    code, so decoding the first 1024 sequences of a 1025-sequence batch gives the same bits as
+    decoding the whole batch."""
     rng = np.random.default_rng(91)
-    lens = rng.integers(0, 700, size=1025)
+    lens = rng.integers(0, 2600, size=1025)
     lens[::97] = 0
-    w = make_workload(lens.tolist(), num_heads=8, num_kv_heads=2, head_dim=64, dtype="bf16", seed=92)
+    w = make_workload(lens.tolist(), num_heads=2, num_kv_heads=1, head_dim=64, dtype="bf16", seed=92)
     _check_inputs(w)
     d = upload(w)
-    out = torch.empty(1025, 8, 64, dtype=torch.float32, device="cuda")
+    out = torch.empty(1025, 2, 64, dtype=torch.float32, device="cuda")
     decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots, d.cow,
-                w.scale, d.k_scale, d.v_scale, partition_tokens=128, variant=2,
-                workspace=workspace_for(d.q, d.k_cache, d.tables, 16, 128), fused=False)
-    out2 = torch.empty(1024, 8, 64, dtype=torch.float32, device="cuda")
+                w.scale, d.k_scale, d.v_scale, partition_tokens=1024, variant=variant,
+                workspace=workspace_for(d.q, d.k_cache, d.tables, 16, 1024), fused=False)
+    out2 = torch.empty(1024, 2, 64, dtype=torch.float32, device="cuda")
     lib.pa_decode(out2, d.q[:1024], d.k_cache, d.v_cache, d.tables[:1024], d.lens[:1024], w.scale,
-                  d.k_scale, d.v_scale, partition_tokens=128, variant=2,
-                  workspace=workspace_for(d.q[:1024], d.k_cache, d.tables[:1024], 16, 128))
+                  d.k_scale, d.v_scale, partition_tokens=1024, variant=variant,
+                  workspace=workspace_for(d.q[:1024], d.k_cache, d.tables[:1024], 16, 1024))
     torch.cuda.synchronize()
     assert torch.equal(out[:1024], out2)
     assert_close(to_numpy_f64(out), run_oracle(w), "bf16", "f32", "1025 sequences, plain grid")
