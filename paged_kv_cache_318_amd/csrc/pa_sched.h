@@ -40,8 +40,18 @@ __device__ __forceinline__ int balanced_groups(long long W, int nw) {
 // finishing together: that batch's kernel took 135.2 us, against 149.1 with equal shares, 144.3 at
 // 24 : 20 : 16, 138.4 at 26 : 20 : 14 and 140.5 at 30 : 20 : 10. The shares depend only on the batch
 // and the CU count, so results stay deterministic.
+// Short shares are not bandwidth-shared long enough for the order to matter, and the heavier
+// first shares then only lengthen the critical path (16 GQA sequences, about 17 bf16 tiles a share:
+// 35.2 us weighted against 28.4 us equal; 4 fp8 sequences, 64 tiles a share: 47.0 against 51.6):
+// the weights apply from kWeightedMinTiles tiles a share on average.
 constexpr int kSlotWeight0 = 28, kSlotWeight1 = 20, kSlotWeight2 = 12;
 constexpr int kSlotWeightSum = kSlotWeight0 + kSlotWeight1 + kSlotWeight2;
+constexpr int kWeightedMinTiles = 48;
+
+// Whether a grid of nw shares over W tiles is the weighted one.
+__device__ __forceinline__ bool weighted_shares(long long W, int nw, int cls) {
+  return cls > 0 && nw == 3 * cls && W >= static_cast<long long>(kWeightedMinTiles) * nw;
+}
 
 // Weight units before work-group i (weighted grid of 3 * cls work-groups).
 __device__ __forceinline__ long long slot_weight_before(int cls, int i) {
@@ -51,16 +61,15 @@ __device__ __forceinline__ long long slot_weight_before(int cls, int i) {
          static_cast<long long>(i - 2 * cls) * kSlotWeight2;  // (i = 3 * cls: the total)
 }
 
-// Work-group i's share starts at tile i*W/nw, or at its weighted place when cls > 0 and the grid is
-// the weighted one (nw == 3 * cls).
+// Work-group i's share starts at tile i*W/nw, or at its weighted place on the weighted grid.
 __device__ __forceinline__ long long share_lo(long long W, int nw, int cls, int i) {
-  if (cls <= 0 || nw != 3 * cls) return (W * i) / nw;
+  if (!weighted_shares(W, nw, cls)) return (W * i) / nw;
   return (W * slot_weight_before(cls, i)) / (static_cast<long long>(cls) * kSlotWeightSum);
 }
 
 // The work-group whose share holds tile t: the largest i with share_lo(i) <= t.
 __device__ __forceinline__ int share_owner(long long W, int nw, int cls, long long t) {
-  if (cls <= 0 || nw != 3 * cls) return static_cast<int>(((t + 1) * nw - 1) / W);
+  if (!weighted_shares(W, nw, cls)) return static_cast<int>(((t + 1) * nw - 1) / W);
   // share_lo(i) <= t  <=>  slot_weight_before(i) <= X, X = floor(((t + 1) * T - 1) / W)
   const long long T = static_cast<long long>(cls) * kSlotWeightSum;
   const long long X = ((t + 1) * T - 1) / W;

@@ -239,10 +239,12 @@ def test_balanced_split_cuts_units(lens, cdt, B):
 
 @pytest.mark.parametrize("cdt", ["bf16", "fp8"])
 def test_balanced_split_weighted_shares(cdt):
-    """A batch long enough for the whole resident grid (three work-groups per CU) gets shares
-    weighted by each work-group's order of arrival on its CU: parity with the oracle, with explicit
-    partitions within tolerance, and the same bits on a second call."""
-    w = make_workload([30000, 20000, 1, 9000], num_heads=16, num_kv_heads=4, head_dim=128,
+    """A batch long enough for the whole resident grid (three work-groups per CU, shares of 48
+    tiles or more) gets shares weighted by each work-group's order of arrival on its CU: parity
+    with the oracle, with explicit partitions within tolerance, and the same bits on a second
+    call."""
+    # 9 501 blocks x 4 kv heads = 38 004 tiles: at least 48 a share over the 768-group grid
+    w = make_workload([72000, 50000, 1, 30000], num_heads=16, num_kv_heads=4, head_dim=128,
                       dtype=cdt, q_dtype="bf16", seed=61)
     ref = run_oracle(w)
     got = run_gpu(w, out_dt="f32", variant=2, fused=False)

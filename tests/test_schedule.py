@@ -4,7 +4,7 @@ The kernels' results are checked on the GPU against the oracle; these tests chec
 arithmetic that decides which work-group reads which tiles, on many shapes at no GPU cost:
 
 * balanced split -- shares (equal, or weighted 28 : 20 : 12 by a work-group's order of arrival on
-  its CU when the grid holds three work-groups per CU) cover the flattened tile list exactly once,
+  its CU when the grid holds three work-groups per CU and the shares average 48 tiles or more) cover the flattened tile list exactly once,
   none is empty, and share_owner -- which the merge kernel uses to find the partial results of a
   unit -- names the share that holds every tile;
 * ordered fixed partitions -- the ordered list holds every (sequence, partition) item exactly once
@@ -18,6 +18,7 @@ import pytest
 
 K_MIN_SHARE_TILES = 16
 W0, W1, W2 = 28, 20, 12
+WEIGHTED_MIN_TILES = 48
 BUCKETS = 16
 
 
@@ -34,14 +35,18 @@ def weight_before(cls, i):
     return cls * (W0 + W1) + (i - 2 * cls) * W2
 
 
+def weighted(W, nw, cls):
+    return cls > 0 and nw == 3 * cls and W >= WEIGHTED_MIN_TILES * nw
+
+
 def share_lo(W, nw, cls, i):
-    if cls <= 0 or nw != 3 * cls:
+    if not weighted(W, nw, cls):
         return (W * i) // nw
     return (W * weight_before(cls, i)) // (cls * (W0 + W1 + W2))
 
 
 def share_owner(W, nw, cls, t):
-    if cls <= 0 or nw != 3 * cls:
+    if not weighted(W, nw, cls):
         return ((t + 1) * nw - 1) // W
     T = cls * (W0 + W1 + W2)
     X = ((t + 1) * T - 1) // W
@@ -68,7 +73,7 @@ def test_balanced_shares_cover_the_tiles_once(cls):
         assert bounds[0] == 0 and bounds[-1] == W
         sizes = [b - a for a, b in zip(bounds, bounds[1:])]
         assert min(sizes) >= 1
-        if nw == 3 * cls and cls:
+        if weighted(W, nw, c):
             # the weighted shares follow the weights (within one tile)
             unit = W / (cls * (W0 + W1 + W2))
             for i, sz in enumerate(sizes):
