@@ -458,7 +458,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.nw = nw;
   a.nw_cls = nw_cls;
   // (the ordered list's 1-D grid must also fit)
+  // (the ordering's length classes multiply a partition's block count by 16 in 32 bits)
   a.ordered = (order_ok && stream_kv && static_cast<int64_t>(pl.part_blocks) * block_size >= kMinOrderedPartition &&
+               pl.part_blocks <= (1 << 26) &&
                units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
   a.k_new = k_new;
   a.v_new = v_new;
