@@ -288,7 +288,7 @@ def test_balanced_split_reuses_one_workspace(cdt):
 @pytest.mark.parametrize("cdt,qdt,B,variant", [("bf16", "bf16", 16, 2), ("fp8", "bf16", 16, 2),
                                               ("bf16", "bf16", 8, 2), ("fp8", "f16", 32, 2),
                                               ("f16", "f16", 16, 1), ("f32", "f32", 16, 1),
-                                              ("fp8", "bf16", 32, 1)])
+                                              ("fp8", "bf16", 32, 1), ("bf16", "bf16", 8, 1)])
 def test_ordered_fixed_partitions(cdt, qdt, B, variant):
     """Fixed partitions of 1024 tokens or more run over the ordered work list (full partitions
     first, then each sequence's last partition by length, empty sequences last), in both decode
