@@ -35,7 +35,6 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ 
   constexpr int CEB = Elem<C_DT>::bytes;
   using CT = typename Store<C_DT>::T;
   __shared__ int s_slot[32];
-  __shared__ int s_whole;
   __shared__ __align__(16) uint8_t tile[128 * 32 * 4];  // [D][B] values of one block, cache type
   const int t0 = blockIdx.x * B, hh = blockIdx.y, tid = threadIdx.x;
   const int nt = T - t0 < B ? T - t0 : B;
@@ -44,28 +43,25 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ 
     s_slot[tid] = (sl < 0 || sl >= NB * B) ? -1 : sl;  // skipped (or out-of-range: ignored)
   }
   __syncthreads();
-  if (tid == 0) {
-    int whole = nt == B && s_slot[0] >= 0 && s_slot[0] % B == 0;
-    for (int i = 1; i < B && whole; ++i) whole = s_slot[i] == s_slot[0] + i;
-    s_whole = whole;
-  }
-  __syncthreads();
+  // whole block in order: B valid slots, the first at a block boundary, each the next
+  const int base = s_slot[0];
+  const bool in_order = tid >= B || (nt == B && base >= 0 && base % B == 0 && s_slot[tid] == base + tid);
+  const bool whole = __syncthreads_and(in_order) != 0;
   const int per_tok = D / 8;                 // 8-dim pieces of one token's head
-  const bool whole = s_whole != 0;
-  for (int w = tid; w < nt * per_tok; w += blockDim.x) {
-    const int i = w / per_tok, d0 = (w - i * per_tok) * 8;
-    const int sl = s_slot[i];
-    if (sl < 0) continue;
-    if (whole)
-      write_piece<IN_DT, C_DT, false>(k_new, v_new, k_cache, v_cache, t0 + i, sl, hh, d0, Hkv, D,
-                                      B, k_scale, v_scale);
-    else
-      write_piece<IN_DT, C_DT, true>(k_new, v_new, k_cache, v_cache, t0 + i, sl, hh, d0, Hkv, D,
-                                     B, k_scale, v_scale);
+  if (!whole) {
+    for (int w = tid; w < nt * per_tok; w += blockDim.x) {
+      const int i = w / per_tok, d0 = (w - i * per_tok) * 8;
+      const int sl = s_slot[i];
+      if (sl < 0) continue;
+      write_piece<IN_DT, C_DT, true>(k_new, v_new, k_cache, v_cache, t0 + i, sl, hh, d0, Hkv, D, B,
+                                     k_scale, v_scale);
+    }
+    return;
   }
-  if (!whole) return;
-  // values of the whole block: token i's 8 dims d0.. land in column i of rows d0..d0+7
-  const int b = s_slot[0] / B;
+  // keys are token rows; values of the whole block go through LDS: token i's 8 dims d0.. land in
+  // column i of rows d0..d0+7. Each piece's value load is issued before its key load, so both
+  // are in flight together.
+  const int b = base / B;
   CT* tl = reinterpret_cast<CT*>(tile);
   float vs = 1.0f;
   if constexpr (C_DT == DT_FP8) vs = v_scale[static_cast<size_t>(b) * Hkv + hh];
@@ -73,6 +69,8 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const void* __restrict__ 
     const int i = w / per_tok, d0 = (w - i * per_tok) * 8;
     const size_t src = (static_cast<size_t>(t0 + i) * Hkv + hh) * D + d0;
     const Raw<8 * IEB> vr = load_raw<8 * IEB>(reinterpret_cast<const uint8_t*>(v_new) + src * IEB);
+    write_piece<IN_DT, C_DT, false>(k_new, v_new, k_cache, v_cache, t0 + i, base + i, hh, d0, Hkv, D,
+                                    B, k_scale, v_scale);
     if constexpr (C_DT == DT_FP8) {
       float vf[8];
       to_f32<IN_DT, 8>(vr.w, vf);
