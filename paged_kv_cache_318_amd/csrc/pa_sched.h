@@ -1,13 +1,16 @@
-// Balanced work split for the decode kernels (device side).
+// Work order of the decode kernels (device side): the balanced split, and the ordered work list
+// of fixed partitions (further below).
 //
-// The batch's work is the flattened list of (sequence, unit, block) tiles, sequence-major: a
-// "unit" is what one work-group accumulates (a query head for the VALU kernel, a kv head with its
-// query group for the MFMA kernel), and unit (s, x) owns nblk(s) consecutive tiles. With W tiles
-// in all and nw work-groups, work-group i takes tiles [i*W/nw, (i+1)*W/nw): every work-group gets
-// the same amount of K/V to read whatever the length mix, so there is no tail of long work-groups.
-// A unit cut by a share boundary is finished by the merge kernel from the partial results of the
-// work-groups that share it (at most two partial results per work-group: its first and its last
-// unit), combined with the same log-sum-exp algebra as the rest of the method.
+// Balanced split. The batch's work is the flattened list of (sequence, unit, block) tiles,
+// sequence-major: a "unit" is what one work-group accumulates (a query head for the VALU kernel, a
+// kv head with its query group for the MFMA kernel), and unit (s, x) owns nblk(s) consecutive
+// tiles. With W tiles in all and nw work-groups, work-group i takes tiles
+// [share_lo(i), share_lo(i+1)): equal shares, or, on a resident grid of three work-groups per CU
+// with long shares, shares weighted by the work-group's order of arrival on its CU (below), so
+// that the work-groups finish together whatever the length mix. A unit cut by a share boundary is
+// finished by the merge kernel from the partial results of the work-groups that share it (at most
+// two partial results per work-group: its first and its last unit), combined with the same
+// log-sum-exp algebra as the rest of the method.
 //
 // Every work-group recomputes the prefix sums of the block counts in LDS from the lengths (no
 // extra launch); work-group 0 also leaves them in the workspace for the merge kernel. The grid
