@@ -545,7 +545,9 @@ template <int CDT, int QDT, int D, int B>
 static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
   const int G = a.num_heads / a.num_kv_heads;
   if (a.grouped) {
-    const dim3 grid(a.num_kv_heads, a.num_groups + a.num_seqs, a.max_parts);
+    // a.max_parts counts a sequence's prefix and own parts together (its slot stride); either kind
+    // alone has at most a.max_parts - 1 parts, so the grid's part dimension stops there
+    const dim3 grid(a.num_kv_heads, a.num_groups + a.num_seqs, a.max_parts - 1 > 0 ? a.max_parts - 1 : 1);
     const size_t shm = mfma_lds_bytes<CDT, D>(16, 0, false);  // up to 16 rows
     if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
     else hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
