@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // The weights are computed once per part into LDS; every thread then sums over parts in the same
 // order (deterministic), with the partial-output loads unrolled.
 constexpr int kMergeChunk = 1024;
-constexpr int kMergeFast = 8;  // units of at most this many parts take the register path
+constexpr int kMergeFast = 16;  // units of at most this many parts take the register path
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block_size) {
