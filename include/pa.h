@@ -174,6 +174,30 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid hipMalloc): the same arguments, plan,
+ * kernels and result bits as pa_decode, but the partial results of split sequences go to a
+ * fixed device array of the library's own (PA_NOALLOC_SCRATCH_BYTES on every GPU the library runs
+ * on, held until the process ends) instead of a caller workspace. The call allocates nothing.
+ *   Returns PA_ERR_WORKSPACE, before any device work, when the plan pa_decode would pick needs more
+ *   than PA_NOALLOC_SCRATCH_BYTES of partial results (pa_decode_workspace_bytes with the same
+ *   partition_tokens bounds the need; a smaller partition count or an explicit partition_tokens
+ *   that keeps the need below the limit avoids it). Otherwise as pa_decode.
+ *   The array is shared by every call on one GPU and nothing in it needs clearing between calls
+ *   (every partial result the merge reads is written by the same call). Calls that overlap on one
+ *   GPU (on different streams, or from different threads without ordering) race on it.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int max_blocks_per_seq, int num_blocks, float scale, pa_dtype q_dtype,
+                      pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
+                      const float* v_scale, int partition_tokens, int variant, int flags,
+                      void* stream);
+
+/*
  * pa_decode_grouped -- pa_decode for a batch whose sequences share prefix blocks (parallel
  * samples of one prompt: [Ultralytics] "シーケンス間でのブロック共有"; [Transcript] the paragraph
  * on shared prefixes), with the shared blocks read once per group instead of once per sequence.

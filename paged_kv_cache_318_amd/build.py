@@ -20,7 +20,7 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["pa_api.cpp", "kv_ops.hip", "decode_valu.hip", "decode_mfma.hip", "prefill_mfma.hip",
-           "diag.hip"]
+           "decode_noalloc.hip", "diag.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -379,7 +379,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 pa_dtype cache_dtype, pa_dtype out_dtype, const float* k_scale,
                 const float* v_scale, int partition_tokens, int variant, int flags,
                 void* workspace, size_t workspace_bytes, void* stream, const void* k_new,
-                const void* v_new, const int32_t* slot_mapping) {
+                const void* v_new, const int32_t* slot_mapping,
+                int (*resolve_workspace)(void**) = nullptr) {
   if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA) return PA_ERR_INVALID_ARG;
   const int status = check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                        num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -425,7 +426,13 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                                 : static_cast<size_t>(num_seqs) * (num_heads / gu) * pl.max_parts;
   const size_t need = balanced ? slot_bytes(slots, gu, head_dim) + (num_seqs + 1) * sizeof(int)
                                : fixed_workspace(num_seqs, num_heads, head_dim, pl);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (need > 0 && workspace_bytes < need) return PA_ERR_WORKSPACE;
+  // a workspace the library provides itself is looked up only now, after every host check
+  if (need > 0 && workspace == nullptr && resolve_workspace != nullptr) {
+    const int ws_status = resolve_workspace(&workspace);
+    if (ws_status != PA_OK) return ws_status;
+  }
+  if (need > 0 && workspace == nullptr) return PA_ERR_WORKSPACE;
 
   pa::DecodeArgs a{};
   a.out = out;
@@ -690,3 +697,26 @@ int pa_profile_read(int kernel_kind, double* total_ms, long long* launches) {
 }
 
 }  // extern "C"
+
+// Not an entry point of the ABI: the allocation-free decode (decode_noalloc.hip) reaches pa_decode's
+// host logic through here.
+namespace pa {
+
+int decode_with_library_workspace(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, float scale,
+                                  int q_dtype, int cache_dtype, int out_dtype,
+                                  const float* k_scale, const float* v_scale, int partition_tokens,
+                                  int variant, int flags, size_t workspace_bytes,
+                                  int (*resolve_workspace)(void**), void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     static_cast<pa_dtype>(q_dtype), static_cast<pa_dtype>(cache_dtype),
+                     static_cast<pa_dtype>(out_dtype), k_scale, v_scale, partition_tokens, variant,
+                     flags, nullptr, workspace_bytes, stream, nullptr, nullptr, nullptr,
+                     resolve_workspace);
+}
+
+}  // namespace pa

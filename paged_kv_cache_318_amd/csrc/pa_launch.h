@@ -32,6 +32,20 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k,
                               const float* src_ks, const float* src_vs, float* dst_ks,
                               float* dst_vs, const int32_t* pairs, int num_pairs, int src_nb,
                               int dst_nb, int Hkv, int D, int B, int cache_dt, hipStream_t st);
+// pa_decode's host logic (validation, plan, launches) with a workspace the library provides:
+// every scalar check runs first; then, if the plan needs more than workspace_bytes, the call
+// returns PA_ERR_WORKSPACE, and otherwise resolve_workspace supplies the workspace's device address
+// (its status is returned if not PA_OK). Defined in pa_api.cpp.
+int decode_with_library_workspace(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, float scale,
+                                  int q_dtype, int cache_dtype, int out_dtype,
+                                  const float* k_scale, const float* v_scale, int partition_tokens,
+                                  int variant, int flags, size_t workspace_bytes,
+                                  int (*resolve_workspace)(void**), void* stream);
+
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                             const int32_t* tables, const int32_t* lens, int num_seqs,
                             int num_kv_heads, int head_dim, int block_size, int max_blocks,

@@ -41,6 +41,8 @@ _SIGS = {
     "pa_decode_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp,
                           _sz, _vp], _i32),
+    "pa_decode_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                           _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
     "pa_decode_grouped_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "pa_decode_grouped": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                            _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32,
@@ -243,6 +245,31 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         S, Hq, Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
         _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), int(flags),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      k_scale=None, v_scale=None, partition_tokens: int = 0,
+                      variant: int = PA_VARIANT_AUTO, stream=None, flags: int = 0) -> None:
+    """pa_decode with the partial results in the library's own fixed device array (no workspace
+    argument, nothing allocated); raises PagedAttnError(PA_ERR_WORKSPACE) when the plan needs more
+    than PA_NOALLOC_SCRATCH_BYTES."""
+    import torch
+    NB, Hkv, B, D = k_cache.shape
+    S, Hq, Dq = q.shape
+    MB = block_tables.shape[1]
+    _need(Dq == D and tuple(out.shape) == (S, Hq, D), "q/out must be [S][Hq][D]")
+    _need(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [NB][Hkv][D][B]")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables / context_lens must be int32")
+    _need(block_tables.shape[0] == S and context_lens.shape[0] == S, "one table row / length per sequence")
+    _check("pa_decode_noalloc", load().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        S, Hq, Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
+        _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(variant), int(flags),
+        _stream(stream)))
+
+
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def pa_decode_grouped_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,

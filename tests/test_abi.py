@@ -48,7 +48,7 @@ def test_header_declares_the_boundary():
     for n in ("pa_write_kv", "pa_decode", "pa_decode_append", "pa_prefill", "pa_copy_blocks",
               "pa_gather_kv",
               "pa_swap_blocks", "pa_decode_grouped", "pa_decode_grouped_workspace_bytes",
-              "pa_decode_workspace_bytes", "pa_status_string"):
+              "pa_decode_workspace_bytes", "pa_status_string", "pa_decode_noalloc"):
         assert n in names
 
 
@@ -109,6 +109,41 @@ def _decode(L, **kw):
 ])
 def test_decode_rejects_bad_arguments(L, kw, want):
     assert _decode(L, **kw) == want
+
+
+def _noalloc(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, S=4, Hq=8, Hkv=8, D=128, B=16,
+             MB=8, NB=64, scale=0.125, qdt=BF16, cdt=BF16, odt=BF16, ks=None, vs=None, part=0,
+             variant=1, flags=0)
+    a.update(kw)
+    return L.pa_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["S"],
+                               a["Hq"], a["Hkv"], a["D"], a["B"], a["MB"], a["NB"], a["scale"],
+                               a["qdt"], a["cdt"], a["odt"], a["ks"], a["vs"], a["part"],
+                               a["variant"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(S=0), INVALID), (dict(Hkv=3), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(variant=5), INVALID), (dict(part=24), INVALID), (dict(flags=2), INVALID),
+    (dict(out=None), INVALID), (dict(D=96), UNSUPPORTED), (dict(cdt=FP8), INVALID),
+    # 64 seqs x 64 heads x 256 partitions of 16 tokens: 545 MB of partial results > the array
+    (dict(S=64, Hq=64, Hkv=64, MB=256, part=16), WORKSPACE),
+])
+def test_decode_noalloc_rejects_bad_arguments(L, kw, want):
+    """Every host check of pa_decode, then the plan's need against PA_NOALLOC_SCRATCH_BYTES, all
+    before any HIP call (the pointers here are never dereferenced)."""
+    assert _noalloc(L, **kw) == want
+
+
+def test_noalloc_limit_matches_the_header(L):
+    text = open(HEADERS[0], encoding="utf-8").read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == palib.PA_NOALLOC_SCRATCH_BYTES
+    # one partition more than fits: 16 heads x P one-block partitions of (D + 2) floats each
+    slots = palib.PA_NOALLOC_SCRATCH_BYTES // ((128 + 2) * 4)
+    P = slots // 16 + 1
+    assert 16 * P * (128 + 2) * 4 > palib.PA_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(L, S=1, Hq=16, Hkv=16, MB=P, part=16) == WORKSPACE
 
 
 def _grouped(L, **kw):
