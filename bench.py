@@ -45,8 +45,11 @@ def parse_args():
     p.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     p.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-also", action="store_true",
+                   help="skip the other decode workloads the headline run also measures")
     p.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of each leg of the oracle timing (all cores, one thread)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
     p.add_argument("--fused", action="store_true",
@@ -279,35 +282,87 @@ def measure_paging(args, lib, torch):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle (as it stands) on host cores, over a bounded sample of the same workload:
-    whole sequences in order until the time budget is spent, BLAS limited to one thread."""
-    import numpy as np
+_CPU_STATE = {}  # the workload and its post-write pools, inherited by the forked workers
+
+
+def host_cores() -> int:
+    """Host cores the CPU baseline may use: the affinity set, capped by the cgroup's CPU quota when
+    one is set and at 16 (the host share of one GPU on a shared node)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(float(quota) / float(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, min(n, 16))
+
+
+def _oracle_pass(seqs, budget_s: float):
+    """Decode the given sequences with the oracle, again and again, until the budget is spent
+    (at least one whole pass); BLAS limited to one thread. Returns (attended tokens, seconds)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
+    w, kp, vp, ks, vs = (_CPU_STATE[k] for k in ("w", "kp", "vp", "ks", "vs"))
+    tokens = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for s in seqs:
+                oracle.decode(w.q, kp, vp, w.tables, w.lens, w.block_size, w.scale, w.dtype,
+                              w.q_dtype, ks, vs, seqs=[s])
+                tokens += int(w.lens[s])
+                if time.perf_counter() - t0 >= budget_s:
+                    return tokens, time.perf_counter() - t0
+            if not seqs:
+                return tokens, time.perf_counter() - t0
 
+
+def cpu_baselines(w, budget_s: float):
+    """The fp64 oracle as it stands, timed on the host over a bounded sample of the same workload:
+    after the step's copies and writes (done once, timed in the 1-thread leg), whole sequences are
+    decoded in turn until the time budget is spent. Two legs: one worker process per host core
+    (forked before the GPU is touched; sequences dealt out longest first, each worker cycling
+    through its own), and one thread. Returns (all-core result, 1-thread result)."""
+    import multiprocessing as mp
+
+    import oracle
+
+    t0 = time.perf_counter()
     kp, vp = w.k_pool.copy(), w.v_pool.copy()
     ks = None if w.k_scale is None else w.k_scale.copy()
     vs = None if w.v_scale is None else w.v_scale.copy()
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.copy_blocks(kp, vp, w.cow, ks, vs)
-        oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs, w.new_dtype)
-        done, tokens = 0, 0
-        while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
-            oracle.decode(w.q, kp, vp, w.tables, w.lens, w.block_size, w.scale, w.dtype, w.q_dtype,
-                          ks, vs, seqs=[done])
-            tokens += int(w.lens[done])
-            done += 1
-        dt = time.perf_counter() - t0
+    oracle.copy_blocks(kp, vp, w.cow, ks, vs)
+    oracle.write_kv(kp, vp, w.k_new, w.v_new, w.slots, w.block_size, w.dtype, ks, vs, w.new_dtype)
+    t_write = time.perf_counter() - t0
+    _CPU_STATE.update(w=w, kp=kp, vp=vp, ks=ks, vs=vs)
     per_tok = w.kv_bytes() / max(w.attended_tokens, 1)
-    gbs = tokens * per_tok / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "attended_tokens_per_s": round(tokens / dt, 1),
-            "sample": f"write of all {w.num_seqs} new tokens + decode of the first {done} of "
-                      f"{w.num_seqs} sequences ({tokens} attended tokens x {w.num_heads} heads), "
-                      f"fp64 numpy, {dt:.1f} s"}
+
+    def result(tokens, dt, cores, sample):
+        return {"value": round(tokens * per_tok / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "kind": "oracle", "attended_tokens_per_s": round(tokens / dt, 1), "sample": sample}
+
+    n = host_cores()
+    order = sorted(range(w.num_seqs), key=lambda s: -int(w.lens[s]))
+    shares = [order[i::n] for i in range(n)]
+    t1 = time.perf_counter()
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.starmap(_oracle_pass, [(sh, budget_s) for sh in shares])
+    wall = time.perf_counter() - t1
+    tok_all = sum(r[0] for r in res)
+    allcore = result(tok_all, wall, n,
+                     f"{n} worker processes (one per host core, BLAS 1 thread each) decoding the "
+                     f"{w.num_seqs} sequences ({w.num_heads} heads) round and round for "
+                     f"{budget_s:.0f} s each: {tok_all} attended tokens in {wall:.1f} s wall, "
+                     f"fp64 numpy, after the step's write")
+    tok1, dt1 = _oracle_pass(list(range(w.num_seqs)), budget_s)
+    one = result(tok1, dt1 + t_write, 1,
+                 f"write of all {w.num_seqs} new tokens + decode of the {w.num_seqs} sequences in "
+                 f"turn for {budget_s:.0f} s ({tok1} attended tokens x {w.num_heads} heads), "
+                 f"fp64 numpy, 1 thread, {dt1 + t_write:.1f} s")
+    _CPU_STATE.clear()
+    return allcore, one
 
 
 def read_ceiling(lib, tile_bytes: int, total_bytes: int = 4 << 30, reps: int = 5):
@@ -380,56 +435,29 @@ def measured_traffic(kernel: str, workload: str, summary: str = "decode_hbm_traf
     return None
 
 
-def main():
-    args = parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "the paged decode path here has no multi-GPU leg; see the design notes on sharding.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    from paged_kv_cache_318_amd import lib
-    from paged_kv_cache_318_amd.step import decode_step, decode_step_grouped, workspace_for
-    from workloads import config
-    from workloads.device import torch_dtype, upload
-
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
-    lib.load()
-    if args.measure == "swap":
-        return measure_swap(args, lib, torch)
-    if args.measure == "paging":
-        return measure_paging(args, lib, torch)
-    if args.measure == "prefill":
-        return measure_prefill(args, lib, torch)
-    over = {}
-    if args.dtype:
-        over["dtype"] = args.dtype
-    if args.first_step:
-        over["first_step"] = True
-    if args.num_seqs > 0:
-        over["num_seqs"] = args.num_seqs
-    t_gen = time.perf_counter()
-    w = config(args.config, **over)
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] workload {w.name}: {w.num_seqs} seqs, {w.attended_tokens} attended tokens, "
-          f"{w.kv_bytes() / 1e9:.3f} GB K/V per call, generated in {t_gen:.1f}s", file=sys.stderr,
-          flush=True)
-
-    # the host knows from its tables whether sequences share physical blocks; if so, pa_decode is
-    # told to read K/V through the caches
+def shared_blocks_flag(w, lib):
+    """PA_DECODE_SHARED_BLOCKS when the host's tables show sequences sharing physical blocks."""
     import numpy as np
     used = np.concatenate([w.tables[s, : -(-int(L) // w.block_size)] for s, L in enumerate(w.lens)])
     shared = bool(used.size) and np.unique(used).size < used.size
-    flags = lib.PA_DECODE_SHARED_BLOCKS if shared else 0
+    return (lib.PA_DECODE_SHARED_BLOCKS if shared else 0), shared
+
+
+def time_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fused=False):
+    """Uploads ``args.replicas`` copies of the workload, runs ``args.warmup`` untimed steps, then
+    three passes of ``args.steps`` steps each: the timed pass (device-synchronised on both sides),
+    a pass with the library's HIP events around every launch (per-kernel averages), and a pass with
+    an event between steps (percentiles). Returns a dict of the measurements."""
+    from paged_kv_cache_318_amd.step import decode_step, decode_step_grouped, workspace_for
+    from workloads.device import torch_dtype, upload
+
+    flags, shared = shared_blocks_flag(w, lib)
     reps = [upload(w) for _ in range(max(1, args.replicas))]
     out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch_dtype(w.q_dtype), device="cuda")
-    ws = workspace_for(reps[0].q, reps[0].k_cache, reps[0].tables, w.block_size, args.partition)
+    ws = workspace_for(reps[0].q, reps[0].k_cache, reps[0].tables, w.block_size, partition)
 
-    grouped = None
-    if args.grouped:
+    gr = None
+    if grouped:
         # sequences sharing prefix blocks (the host's tables say which) decode through
         # pa_decode_grouped, each shared block read once per group
         from paged_kv_cache_318_amd.blocks import shared_prefix_groups
@@ -437,29 +465,27 @@ def main():
         mg = max(1, 16 // G)
         gs, pref = shared_prefix_groups(w.tables, w.lens, w.block_size, mg)
         gws = torch.empty(lib.pa_decode_grouped_workspace_bytes(
-            w.num_seqs, w.num_heads, w.head_dim, w.tables.shape[1], w.block_size, args.partition),
+            w.num_seqs, w.num_heads, w.head_dim, w.tables.shape[1], w.block_size, partition),
             dtype=torch.uint8, device="cuda")
-        grouped = (torch.from_numpy(gs).cuda(), torch.from_numpy(pref).cuda(), mg, gws,
-                   len(gs) - 1, int(pref.max(initial=0)))
+        gr = {"gs": torch.from_numpy(gs).cuda(), "pref": torch.from_numpy(pref).cuda(), "mg": mg,
+              "ws": gws, "groups": len(gs) - 1, "max_prefix_blocks": int(pref.max(initial=0))}
 
     def step(i):
         d = reps[i % len(reps)]
-        if grouped is not None:
+        if gr is not None:
             decode_step_grouped(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new,
-                                d.slots, d.cow, grouped[0], grouped[1], grouped[2], w.scale,
-                                d.k_scale, d.v_scale, partition_tokens=args.partition,
-                                workspace=grouped[3], flags=flags)
+                                d.slots, d.cow, gr["gs"], gr["pref"], gr["mg"], w.scale,
+                                d.k_scale, d.v_scale, partition_tokens=partition,
+                                workspace=gr["ws"], flags=flags)
             return
         decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
-                    d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=args.partition,
-                    variant=args.variant, workspace=ws, flags=flags, fused=args.fused)
-
-    calibration_copy(args, torch)
+                    d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=partition,
+                    variant=variant, workspace=ws, flags=flags, fused=fused)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    print(f"[bench] warmup of {args.warmup} steps done", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: warmup of {args.warmup} steps done", file=sys.stderr, flush=True)
 
     # timed region: K steps, nothing else on the stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -478,10 +504,12 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms_step_profiled = start.elapsed_time(end) / args.steps
-    k_ms, k_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_PARTITION)
-    m_ms, m_n = lib.pa_profile_read(lib.PA_KERNEL_DECODE_MERGE)
-    w_ms, w_n = lib.pa_profile_read(lib.PA_KERNEL_WRITE_KV)
-    c_ms, c_n = lib.pa_profile_read(lib.PA_KERNEL_COPY_BLOCKS)
+    kern = {}
+    for name, kind in (("decode_partition", lib.PA_KERNEL_DECODE_PARTITION),
+                       ("decode_merge", lib.PA_KERNEL_DECODE_MERGE),
+                       ("write_kv", lib.PA_KERNEL_WRITE_KV), ("copy_blocks", lib.PA_KERNEL_COPY_BLOCKS)):
+        ms, n = lib.pa_profile_read(kind)
+        kern[name] = (ms / n) if n else None
     lib.pa_profile_enable(False)
     # a third pass with an event before every step and after the last: the spread of step times
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -495,19 +523,120 @@ def main():
     def pct(q):
         return round(per_step[min(len(per_step) - 1, int(q * (len(per_step) - 1) + 0.5))], 2)
 
-    step_pcts = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
-    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-
-    step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    k_avg_ms = k_ms / max(k_n, 1)
+    print(f"[bench] {w.name}: timed {args.steps} steps, {ms_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
     G = w.num_heads // w.num_kv_heads
     mfma_ok = w.dtype != "f32" and G <= 16
-    kernel = "decode_mfma" if (args.grouped or args.variant == 2 or
-                               (args.variant == 0 and mfma_ok and G >= 2)) else "decode_valu"
+    kernel = "decode_mfma" if (grouped or variant == 2 or (variant == 0 and mfma_ok and G >= 2)) \
+        else "decode_valu"
+    del reps, out, ws
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "ms_step_profiled": ms_step_profiled, "kernels_ms": kern,
+            "pcts": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}, "kernel": kernel,
+            "shared": shared, "grouped": None if gr is None else
+            {"groups": gr["groups"], "max_prefix_blocks": gr["max_prefix_blocks"]}}
+
+
+def us(ms):
+    return None if ms is None else round(1e3 * ms, 2)
+
+
+def decode_roofline(w, m, unique):
+    """Achieved algorithmic GB/s of the attention kernel (average launch) and its fraction of the
+    8 TB/s HBM peak."""
+    dec = w.decode_bytes(unique=unique)
+    achieved = dec / (m["kernels_ms"]["decode_partition"] * 1e-3) / 1e9
+    return dec, achieved, achieved / HBM_PEAK_GBS
+
+
+# The other workloads the decode kernels are held to, measured in the same run and the same way
+# as the headline line: (label, config, overrides, grouped decode, bytes basis unique).
+ALSO = (("cfg2-opt13b-mha-bf16", 2, {"dtype": "bf16"}, False, False),
+        ("cfg3-gqa-long-bf16", 3, {}, False, False),
+        ("cfg5-fp8-kv", 5, {}, False, False),
+        ("cfg4-shared-prefix-bf16-grouped", 4, {}, True, True))
+
+
+def measure_also(args, lib, torch, config):
+    res = {}
+    for label, n, over, grouped, unique in ALSO:
+        t0 = time.perf_counter()
+        w = config(n, **over)
+        gen = time.perf_counter() - t0
+        m = time_steps(w, args, lib, torch, grouped=grouped)
+        dec, achieved, frac = decode_roofline(w, m, unique)
+        step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
+        res[label] = {
+            "kernel": m["kernel"], "decode": "pa_decode_grouped" if grouped else "pa_decode",
+            "attention_kernel_us": us(m["kernels_ms"]["decode_partition"]),
+            "merge_us": us(m["kernels_ms"]["decode_merge"]),
+            "write_kv_us": us(m["kernels_ms"]["write_kv"]),
+            "copy_blocks_us": us(m["kernels_ms"]["copy_blocks"]),
+            "step_us": round(1e3 * m["ms_step"], 2), "step_us_percentiles": m["pcts"],
+            "bytes_per_launch": dec, "bytes_basis": "unique" if unique else "logical",
+            "achieved_gbs": round(achieved, 2), "frac": round(frac, 4),
+            "step_gbs": round(step_bytes / (m["ms_step"] * 1e-3) / 1e9, 2),
+            "attended_tokens_per_s": round(w.attended_tokens / (m["ms_step"] * 1e-3), 1),
+            "cache_dtype": w.dtype, "num_seqs": w.num_seqs, "attended_tokens": w.attended_tokens,
+        }
+        print(f"[bench] also {label}: attention kernel {res[label]['attention_kernel_us']} us, "
+              f"frac {res[label]['frac']} (generated in {gen:.1f}s)", file=sys.stderr, flush=True)
+        del w
+    return res
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the paged decode path here has no multi-GPU leg; see the design notes on sharding.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_318_amd import lib
+    from workloads import config
+
+    # (counting devices does not initialise the GPU; the CPU baseline below forks before it is)
+    assert torch.cuda.device_count() > 0, "bench.py needs the GPU"
+    if args.measure != "step":
+        assert torch.cuda.is_available(), "bench.py needs the GPU"
+        lib.load()
+        return {"swap": measure_swap, "paging": measure_paging,
+                "prefill": measure_prefill}[args.measure](args, lib, torch)
+    over = {}
+    if args.dtype:
+        over["dtype"] = args.dtype
+    if args.first_step:
+        over["first_step"] = True
+    if args.num_seqs > 0:
+        over["num_seqs"] = args.num_seqs
+    t_gen = time.perf_counter()
+    w = config(args.config, **over)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] workload {w.name}: {w.num_seqs} seqs, {w.attended_tokens} attended tokens, "
+          f"{w.kv_bytes() / 1e9:.3f} GB K/V per call, generated in {t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baselines(w, args.cpu_seconds)
+        print(f"[bench] oracle: {cpu[0]['value']} GB/s on {cpu[0]['cores']} cores, "
+              f"{cpu[1]['value']} GB/s on 1", file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    lib.load()
+    calibration_copy(args, torch)
+    m = time_steps(w, args, lib, torch, grouped=args.grouped, variant=args.variant,
+                   partition=args.partition, fused=args.fused)
+    ms_step = m["ms_step"]
+    step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
+    value = step_bytes / (ms_step * 1e-3) / 1e9
     unique = args.config == 4
-    dec_bytes = w.decode_bytes(unique=unique)
-    achieved = dec_bytes / (k_avg_ms * 1e-3) / 1e9
+    dec_bytes, achieved, frac = decode_roofline(w, m, unique)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -531,37 +660,37 @@ def main():
             "cow_pairs": int(w.cow.shape[0]), "step_bytes": step_bytes,
             "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
             "replicas": args.replicas, "partition_tokens": args.partition, "variant": args.variant,
-            "shared_blocks_flag": shared,
+            "shared_blocks_flag": m["shared"],
             "write": "fused into the attention (pa_decode_append)" if args.fused
                      else "separate launch (pa_write_kv, then pa_decode)",
-            "grouped": None if grouped is None else {"groups": grouped[4], "max_prefix_blocks": grouped[5]},
+            "grouped": m["grouped"],
         },
         "kernels_us": {
-            "step_with_events": round(1e3 * ms_step_profiled, 2),
-            "decode_partition": round(1e3 * k_avg_ms, 2),
-            "decode_merge": round(1e3 * m_ms / max(m_n, 1), 2) if m_n else None,
-            "write_kv": round(1e3 * w_ms / max(w_n, 1), 2) if w_n else None,
-            "copy_blocks": round(1e3 * c_ms / max(c_n, 1), 2) if c_n else None,
+            "step_with_events": round(1e3 * m["ms_step_profiled"], 2),
+            "decode_partition": us(m["kernels_ms"]["decode_partition"]),
+            "decode_merge": us(m["kernels_ms"]["decode_merge"]),
+            "write_kv": us(m["kernels_ms"]["write_kv"]),
+            "copy_blocks": us(m["kernels_ms"]["copy_blocks"]),
         },
-        "step_us_percentiles": step_pcts,
+        "step_us_percentiles": m["pcts"],
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernel, w.name),
-            "kernel": kernel, "bytes_per_launch": dec_bytes,
+            "frac": round(frac, 4),
+            "traffic": measured_traffic(m["kernel"], w.name),
+            "kernel": m["kernel"], "bytes_per_launch": dec_bytes,
             "bytes_basis": "unique" if unique else "logical",
         },
-        "cpu_baseline": None,
+        "cpu_baseline": None if cpu is None else cpu[0],
+        "cpu_baseline_1t": None if cpu is None else cpu[1],
     }
+    del w
+    if not args.no_also and args.config == 2 and not over:
+        line["also"] = measure_also(args, lib, torch, config)
     if not args.no_ceiling:
-        del reps
-        ceil = read_ceiling(lib, w.block_size * w.head_dim * (1 if w.dtype == "fp8" else 2) *
-                            (2 if w.dtype == "f32" else 1))
+        ceil = read_ceiling(lib, line["config"]["block_size"] * line["config"]["head_dim"] *
+                            (1 if line["dtype"] == "fp8" else 2) * (2 if line["dtype"] == "f32" else 1))
         line["read_ceiling_gbs"] = ceil
         line["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["scattered"], 4)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -587,26 +587,36 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, int 
   return hipErrorInvalidValue;
 }
 
-// Work-groups per CU the balanced kernel keeps resident (from the occupancy calculator).
-int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S, bool stream_kv) {
-  int n = 0;
-  const void* k = nullptr;
-#define PA_PICK(C, Q, DD, BB)                                                                       \
-  if (cdt == C && qdt == Q && D == DD && B == BB)                                                   \
-    k = stream_kv ? reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, true>) \
-                  : reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, false>);
+// Work-groups per CU the balanced kernel keeps resident (from the occupancy calculator): the
+// smaller of its two cache-policy instances, so that the plan -- and with it the result bits --
+// never depends on the PA_DECODE_SHARED_BLOCKS hint.
+int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S) {
+  const void* k[2] = {nullptr, nullptr};
+#define PA_PICK(C, Q, DD, BB)                                                              \
+  if (cdt == C && qdt == Q && D == DD && B == BB) {                                        \
+    k[0] = reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, true>);  \
+    k[1] = reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, false>); \
+  }
 #define PA_PICK_B(C, Q, DD) PA_PICK(C, Q, DD, 8) PA_PICK(C, Q, DD, 16) PA_PICK(C, Q, DD, 32)
   PA_PICK_B(DT_F16, DT_F16, 64) PA_PICK_B(DT_F16, DT_F16, 128) PA_PICK_B(DT_BF16, DT_BF16, 64)
   PA_PICK_B(DT_BF16, DT_BF16, 128) PA_PICK_B(DT_FP8, DT_F16, 64) PA_PICK_B(DT_FP8, DT_F16, 128)
   PA_PICK_B(DT_FP8, DT_BF16, 64) PA_PICK_B(DT_FP8, DT_BF16, 128)
 #undef PA_PICK_B
 #undef PA_PICK
-  if (k == nullptr) return 0;
+  if (k[0] == nullptr) return 0;
   size_t shm = 0;
   if (cdt == DT_FP8) shm = D == 64 ? mfma_lds_bytes<DT_FP8, 64>(G, S, true) : mfma_lds_bytes<DT_FP8, 128>(G, S, true);
   else shm = D == 64 ? mfma_lds_bytes<DT_BF16, 64>(G, S, true) : mfma_lds_bytes<DT_BF16, 128>(G, S, true);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, shm) != hipSuccess) return 0;
-  return n;
+  int best = 0;
+  for (int i = 0; i < 2; ++i) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k[i], 256, shm) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    best = i == 0 ? n : (n < best ? n : best);
+  }
+  return best;
 }
 
 }  // namespace pa

@@ -50,6 +50,9 @@ constexpr int kFewUnits = 256;
 constexpr int kManyUnitsOrdered = 1024;
 constexpr int kDefaultPartitionMfmaOrderedMany = 2048;
 constexpr int kMaxGridYZ = 65535;
+// HIP bounds gridDim.x * blockDim.x by 2^32 - 1 work-items: at most this many work-groups of 256
+// threads (the widest block any kernel here launches) along x.
+constexpr int64_t kMaxGridX = int64_t{0xFFFFFFFF} / 256;
 
 bool dtype_ok(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
@@ -206,6 +209,8 @@ int pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cac
   if (in_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (cache_dtype != PA_FP8_E4M3 && cache_dtype != in_dtype) return PA_ERR_UNSUPPORTED;
   if (num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(num_tokens) + block_size - 1) / block_size > kMaxGridX)
+    return PA_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
@@ -227,6 +232,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
   if (!dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (num_pairs > kMaxGridX) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
   if (cache_dtype == PA_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
@@ -252,6 +258,7 @@ int pa_swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
   if (!dtype_ok(cache_dtype)) return PA_ERR_INVALID_ARG;
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
+  if (num_pairs > kMaxGridX) return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;
   const bool fp8 = cache_dtype == PA_FP8_E4M3;
   if (!k_cache || !v_cache || !host_k || !host_v || !block_pairs) return PA_ERR_INVALID_ARG;
@@ -307,6 +314,8 @@ int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_ca
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size >= (int64_t{1} << 31)) return PA_ERR_INVALID_ARG;
   if (max_tokens > max_blocks_per_seq * block_size) return PA_ERR_INVALID_ARG;
   if (num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(max_tokens) + block_size - 1) / block_size > kMaxGridX)
+    return PA_ERR_UNSUPPORTED;
   if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -410,11 +419,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   const bool order_ok = !balanced && num_seqs <= pa::kOrderedMaxSeqs;
   const Plan pl = plan_partitions(max_blocks_per_seq, block_size, partition_tokens, use_mfma, units,
                                   order_ok);
-  if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ || pl.max_parts > kMaxGridYZ || num_heads > kMaxGridX)
+    return PA_ERR_UNSUPPORTED;
   int nw = 0, nw_cls = 0;
   if (balanced) {
-    const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs,
-                                              stream_kv);
+    const int per_cu = pa::mfma_groups_per_cu(cache_dtype, q_dtype, head_dim, block_size, G, num_seqs);
     const int cus = cu_count();
     nw = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
     nw = nw > pa::kMaxBalancedGroups ? pa::kMaxBalancedGroups : nw;
@@ -464,11 +473,10 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.balanced = balanced ? 1 : 0;
   a.nw = nw;
   a.nw_cls = nw_cls;
-  // (the ordered list's 1-D grid must also fit)
-  // (the ordering's length classes multiply a partition's block count by 16 in 32 bits)
+  // (the ordered list's 1-D grid must also fit, else the 3-D grid takes the batch; the
+  // ordering's length classes multiply a partition's block count by 16 in 32 bits)
   a.ordered = (order_ok && stream_kv && static_cast<int64_t>(pl.part_blocks) * block_size >= kMinOrderedPartition &&
-               pl.part_blocks <= (1 << 26) &&
-               units * pl.max_parts < (int64_t{1} << 31)) ? 1 : 0;
+               pl.part_blocks <= (1 << 26) && units * pl.max_parts <= kMaxGridX) ? 1 : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_slots = k_new != nullptr ? slot_mapping : nullptr;
@@ -536,7 +544,8 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
   if (static_cast<int64_t>(max_group_size) * G > 16) return PA_ERR_UNSUPPORTED;
   if (!group_start || !prefix_blocks) return PA_ERR_INVALID_ARG;
   const Plan pl = grouped_plan(max_blocks_per_seq, block_size, partition_tokens);
-  if (static_cast<int64_t>(num_seqs) + num_groups > kMaxGridYZ || pl.max_parts > kMaxGridYZ)
+  if (static_cast<int64_t>(num_seqs) + num_groups > kMaxGridYZ || pl.max_parts > kMaxGridYZ ||
+      num_heads > kMaxGridX)
     return PA_ERR_UNSUPPORTED;
   const size_t need = grouped_workspace(num_seqs, num_heads, head_dim, pl);
   if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
@@ -636,7 +645,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (out_dtype != q_dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
   const int G = num_heads / num_kv_heads;
   // one work-group per (64-row tile, kv head, sequence), in a one-dimensional grid
-  if ((static_cast<int64_t>(max_query_len) * G + 63) / 64 * num_kv_heads * num_seqs >= (int64_t{1} << 31))
+  if ((static_cast<int64_t>(max_query_len) * G + 63) / 64 * num_kv_heads * num_seqs > kMaxGridX)
     return PA_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_INVALID_ARG;

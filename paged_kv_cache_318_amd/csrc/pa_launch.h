@@ -13,9 +13,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int cache_dt, int q_dt, int h
                               int block_size, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,
                               int block_size, hipStream_t st);
-// Work-groups per CU the balanced MFMA kernel keeps resident (0 if unknown).
+// Work-groups per CU the balanced MFMA kernel keeps resident, whatever its cache policy (0 if
+// unknown).
 int mfma_groups_per_cu(int cache_dt, int q_dt, int head_dim, int block_size, int group,
-                       int num_seqs, bool stream_kv);
+                       int num_seqs);
 hipError_t launch_prefill(const PrefillArgs& a, int cache_dt, int q_dt, int head_dim, int block_size,
                           int max_query_len, hipStream_t st);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, hipStream_t st);

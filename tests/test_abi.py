@@ -106,6 +106,8 @@ def _decode(L, **kw):
     (dict(MB=128, part=512), WORKSPACE),                              # 4 partitions need workspace
     (dict(MB=128, part=512, ws=FAKE, wsb=100), WORKSPACE),
     (dict(S=70000), UNSUPPORTED),
+    # the 3-D grid's x (query heads, or kv heads) and the merge's: at most (2^32 - 1) / 256
+    (dict(Hq=1 << 24, Hkv=1 << 24), UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments(L, kw, want):
     assert _decode(L, **kw) == want
@@ -193,6 +195,7 @@ def _write(L, **kw):
     (dict(D=100), UNSUPPORTED), (dict(B=64), UNSUPPORTED), (dict(idt=F16, cdt=BF16), UNSUPPORTED),
     (dict(idt=FP8, cdt=FP8), UNSUPPORTED), (dict(cdt=FP8), INVALID), (dict(kn=None), INVALID),
     (dict(T=0, kn=None, slots=None), OK),                              # empty write: no-op
+    (dict(T=8 * 16777215 + 1, B=8), UNSUPPORTED),  # one work-group per 8 tokens: 2^24 > grid max
 ])
 def test_write_kv_rejects_bad_arguments(L, kw, want):
     assert _write(L, **kw) == want
@@ -209,6 +212,7 @@ def _copy(L, **kw):
     (dict(n=-1), INVALID), (dict(Hkv=0), INVALID), (dict(D=32), UNSUPPORTED),
     (dict(cdt=FP8), INVALID), (dict(pairs=None), INVALID), (dict(cdt=11), INVALID),
     (dict(n=0, pairs=None, kc=None), OK),
+    (dict(n=1 << 24), UNSUPPORTED),                # one work-group row per pair: past the grid
 ])
 def test_copy_blocks_rejects_bad_arguments(L, kw, want):
     assert _copy(L, **kw) == want
@@ -229,6 +233,7 @@ def _swap(L, **kw):
     (dict(hk=None), INVALID), (dict(pairs=None), INVALID), (dict(cdt=FP8), INVALID),
     (dict(cdt=FP8, ks=FAKE, vs=FAKE), INVALID), (dict(NB=1 << 28), INVALID),
     (dict(n=0, pairs=None, kc=None, hk=None), OK),
+    (dict(n=1 << 24), UNSUPPORTED),
 ])
 def test_swap_blocks_rejects_bad_arguments(L, kw, want):
     """Scalar and null-pointer checks (all before any HIP call); the pointer-kind checks need the
@@ -277,6 +282,8 @@ def _prefill(L, **kw):
     (dict(qdt=F32, cdt=F32, odt=F32), UNSUPPORTED),
     (dict(qdt=F16), UNSUPPORTED), (dict(odt=F16), UNSUPPORTED), (dict(cdt=FP8, qdt=FP8), UNSUPPORTED),
     (dict(S=70000, mql=1 << 20), UNSUPPORTED), (dict(qs=None), INVALID), (dict(out=None), INVALID),
+    # one work-group per 64-row tile, kv head and sequence: 2^24 work-groups is one past the grid
+    (dict(S=1, Hq=1, Hkv=1, mql=1 << 30), UNSUPPORTED),
     (dict(cdt=FP8), INVALID), (dict(cdt=FP8, ks=FAKE), INVALID),
     (dict(T=0, out=None, q=None, kc=None, vc=None, tab=None, lens=None, qs=None, mql=0), OK),
 ])
@@ -290,6 +297,9 @@ def test_gather_rejects_bad_arguments(L):
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 128, 16, 4, 64, 64, F16, None) == INVALID
     assert g(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 16, 4, 64, 64, F16, None) == INVALID
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 80, 16, 4, 64, 64, F16, None) == UNSUPPORTED
+    # one work-group per block of tokens read back: 2^24 blocks is one past the grid's x limit
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 8, 1 << 24, 64, 8 << 24, F16,
+             None) == UNSUPPORTED
 
 
 def test_profile_counters_without_launches(L):

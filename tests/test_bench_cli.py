@@ -25,3 +25,16 @@ def test_help_lists_the_measurements():
     assert p.returncode == 0
     for word in ("--config", "--measure", "--fused", "--grouped", "--partition"):
         assert word in p.stdout
+
+
+def test_cpu_baseline_legs_on_the_tiny_workload():
+    """The oracle's two timing legs (one worker process per host core, and one thread) run on a
+    small workload and report their core counts and rates."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import config
+    allcore, one = bench.cpu_baselines(config(1), 0.2)
+    assert 1 <= allcore["cores"] <= 16 and one["cores"] == 1
+    for r in (allcore, one):
+        assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+        assert r["value"] > 0 and r["attended_tokens_per_s"] > 0

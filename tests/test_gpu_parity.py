@@ -329,6 +329,56 @@ def test_ordered_grid_matches_the_plain_grid_bit_for_bit(variant):
     assert_close(to_numpy_f64(out), run_oracle(w), "bf16", "f32", "1025 sequences, plain grid")
 
 
+def test_wide_table_past_the_one_dimensional_grid_limit():
+    """The ordered grid is one-dimensional: one work-group per (unit, partition of the table's
+    width). HIP bounds a grid's x extent by 2^32 - 1 work-items, 2^24 - 1 work-groups of 256
+    threads. 1024 sequences x 2048 heads with a table 8 partitions of 2048 tokens wide need exactly
+    2^24, so the batch takes the (head, sequence, partition) grid instead. Its result equals, bit
+    for bit, the same batch with a one-partition table (which runs on the ordered grid), and the
+    oracle on sampled sequences. Short lengths (one block each) keep the work small; K/V/q are
+    drawn on the GPU from a seeded generator and the sampled blocks read back for the oracle."""
+    S, H, D, B, P = 1024, 2048, 64, 16, 2048
+    wide, narrow = 8 * P // B, P // B
+    assert S * H * (wide * B // P) == 1 << 24
+    rng = np.random.default_rng(93)
+    lens = rng.integers(1, B + 1, size=S).astype(np.int32)      # one block per sequence
+    NB = S + S // 5
+    first = rng.permutation(NB)[:S].astype(np.int32)
+    tw = np.full((S, wide), -1, np.int32)
+    tw[:, 0] = first
+    tn = np.ascontiguousarray(tw[:, :narrow])
+    assert first.min() >= 0 and first.max() < NB and lens.max() <= B   # every index in bounds
+    print(f"case: wide table, {S} seqs x {H} heads x D {D}, {wide} blocks wide", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(94)
+    k = torch.randn(NB, H, B, D, generator=g, device="cuda", dtype=torch.float16)
+    v = torch.randn(NB, H, D, B, generator=g, device="cuda", dtype=torch.float16)
+    q = torch.randn(S, H, D, generator=g, device="cuda", dtype=torch.float16)
+    lens_d = torch.from_numpy(lens).cuda()
+    tw_d, tn_d = torch.from_numpy(tw).cuda(), torch.from_numpy(tn).cuda()
+    scale = D ** -0.5
+    out_w = torch.empty(S, H, D, dtype=torch.float32, device="cuda")
+    out_n = torch.empty_like(out_w)
+    ws = workspace_for(q, k, tw_d, B, P)
+    assert ws is not None and ws.numel() == S * H * 8 * (D + 2) * 4
+    lib.pa_decode(out_w, q, k, v, tw_d, lens_d, scale, partition_tokens=P, workspace=ws)
+    assert workspace_for(q, k, tn_d, B, P) is None
+    lib.pa_decode(out_n, q, k, v, tn_d, lens_d, scale, partition_tokens=P)
+    torch.cuda.synchronize()
+    del ws
+    assert torch.equal(out_w, out_n)
+    samp = np.unique(np.concatenate([[0, 1, S // 2, S - 1], rng.integers(0, S, size=4)]))
+    blocks = torch.from_numpy(first[samp].astype(np.int64)).cuda()
+    kb = k.index_select(0, blocks).cpu().numpy()
+    vb = v.index_select(0, blocks).cpu().numpy()
+    tab = np.arange(samp.size, dtype=np.int32)[:, None]
+    ref = oracle.decode(q[torch.from_numpy(samp).cuda()].cpu().numpy(), kb, vb, tab, lens[samp], B,
+                        scale, "f16")
+    got = to_numpy_f64(out_w.index_select(0, torch.from_numpy(samp).cuda()))
+    assert_close(got, ref, "f16", "f32", "wide table, sampled sequences")
+    del k, v, q, out_w, out_n
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,D,B,variant", COMBOS)
 @pytest.mark.parametrize("part", [0, 256])
 def test_separate_write_and_decode_parity(cdt, qdt, hq, hkv, D, B, variant, part):
@@ -402,11 +452,15 @@ def test_fused_step_skips_slots_that_are_not_the_last_position(variant, cdt):
 
 @pytest.mark.parametrize("cdt,qdt,hq,hkv,variant", [("f16", "f16", 4, 4, 1), ("bf16", "bf16", 8, 2, 2),
                                                     ("fp8", "bf16", 8, 2, 2), ("fp8", "f16", 4, 4, 1)])
-def test_shared_blocks_flag_is_only_a_cache_hint(cdt, qdt, hq, hkv, variant):
+@pytest.mark.parametrize("part", [256, 0])
+def test_shared_blocks_flag_is_only_a_cache_hint(cdt, qdt, hq, hkv, variant, part):
+    """Same bits with and without PA_DECODE_SHARED_BLOCKS, with fixed partitions and with the
+    default plan (for the few-unit MFMA batches here: the balanced split, whose grid size comes
+    from the kernel's occupancy)."""
     w = make_workload(list(SMALL_LENS), num_heads=hq, num_kv_heads=hkv, head_dim=128, dtype=cdt,
                       q_dtype=qdt, seed=77)
-    a = run_gpu(w, out_dt="f32", part=256, variant=variant)
-    b = run_gpu(w, out_dt="f32", part=256, variant=variant, flags=lib.PA_DECODE_SHARED_BLOCKS)
+    a = run_gpu(w, out_dt="f32", part=part, variant=variant)
+    b = run_gpu(w, out_dt="f32", part=part, variant=variant, flags=lib.PA_DECODE_SHARED_BLOCKS)
     assert np.array_equal(a, b)
     assert_close(b, run_oracle(w), cdt, "f32", "shared-blocks flag")
 
