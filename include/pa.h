@@ -27,6 +27,15 @@
  *   q, out        [num_seqs][num_heads][head_dim]
  *   query head h reads kv head h / (num_heads / num_kv_heads).
  *
+ * Where this interface goes beyond the plain statement of the problem (a query, the shared K/V
+ * block pools, per-sequence block tables, context lengths, the block size and the scale):
+ *   - values are stored dim-major inside a block (v_cache above); the pages fix only a one-head
+ *     [block][slot][dim] key pool, and keys keep that order;
+ *   - pa_decode takes three more ints: partition_tokens (split length, 0 = the library's plan),
+ *     variant (kernel choice) and flags (a cache hint); pa_decode_workspace_bytes takes
+ *     num_kv_heads and partition_tokens, on which the plan depends;
+ *   - streams are passed as void* (a hipStream_t), so this header needs no HIP include.
+ *
  * Element types: PA_F32 (IEEE binary32), PA_F16 (binary16), PA_BF16 (bfloat16 bit patterns),
  * PA_FP8_E4M3 (OCP E4M3: bias 7, max 448, no infinities, S.1111.111 = NaN).
  *

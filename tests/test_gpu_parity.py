@@ -45,14 +45,21 @@ def _half_ulp(x, dt):
 
 
 def assert_close(got, want, cache_dt, out_dt, what=""):
+    """Max-abs error within the cache dtype's tolerance. A 16-bit output must itself be rounded:
+    where |o_ref| >= 1 its half ulp exceeds the 16-bit tolerance's margin (bf16: 2^-8 at 1), so
+    there an element may also be off by half an ulp of the output type; the number of elements
+    that needed that allowance is printed."""
     assert got.shape == want.shape
-    tol = TOL[cache_dt] + _half_ulp(want, out_dt)
+    allow = np.where(np.abs(want) >= 1.0, _half_ulp(want, out_dt), 0.0)
     err = np.abs(got - want)
-    bad = ~(err <= tol)
+    bad = ~(err <= TOL[cache_dt] + allow)
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(np.isfinite(err), err, np.inf)), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; max err "
                              f"{np.nanmax(err):.3e} at {i} (got {got[i]}, want {want[i]})")
+    if out_dt != "f32":
+        print(f"[half-ulp allowance] {what}: {int((err > TOL[cache_dt]).sum())} of {err.size} "
+              f"{out_dt} outputs ({int((np.abs(want) >= 1.0).sum())} with |o_ref| >= 1)")
     return float(err.max()) if err.size else 0.0
 
 

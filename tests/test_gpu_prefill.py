@@ -45,9 +45,16 @@ def _half_ulp(ref, out_dt):
 
 
 def assert_close(got, want, cache_dt, out_dt, what=""):
+    """Max-abs error within the cache dtype's tolerance, plus half an ulp of a 16-bit output type
+    where |o_ref| >= 1 (there the output's own rounding exceeds the tolerance's margin); the number
+    of elements that needed that allowance is printed."""
     assert got.shape == want.shape
     err = np.abs(got - want)
-    bad = ~(err <= TOL[cache_dt] + _half_ulp(want, out_dt))
+    allow = np.where(np.abs(want) >= 1.0, _half_ulp(want, out_dt), 0.0)
+    bad = ~(err <= TOL[cache_dt] + allow)
+    if out_dt != "f32" and not bad.any():
+        print(f"[half-ulp allowance] {what}: {int((err > TOL[cache_dt]).sum())} of {err.size} "
+              f"{out_dt} outputs ({int((np.abs(want) >= 1.0).sum())} with |o_ref| >= 1)")
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(np.isfinite(err), err, np.inf)), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; max err "

@@ -12,14 +12,38 @@ arithmetic that decides which work-group reads which tiles, on many shapes at no
   first, and the grid covers it.
 """
 
+import os
 import random
+import re
 
 import pytest
 
-K_MIN_SHARE_TILES = 16
-W0, W1, W2 = 28, 20, 12
-WEIGHTED_MIN_TILES = 48
-BUCKETS = 16
+SCHED_H = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "paged_kv_cache_318_amd", "csrc", "pa_sched.h")
+
+
+def _device_constants():
+    """The integer constants the device code uses (``constexpr int kName = <int>;`` lines of
+    pa_sched.h), so that this model and the kernels cannot drift apart."""
+    text = open(SCHED_H, encoding="utf-8").read()
+    out = {}
+    for decl in re.findall(r"constexpr\s+int\s+([^;]*);", text):
+        for name, value in re.findall(r"(k\w+)\s*=\s*(\d+)", decl):
+            out[name] = int(value)
+    return out
+
+
+_C = _device_constants()
+K_MIN_SHARE_TILES = _C["kMinShareTiles"]
+W0, W1, W2 = _C["kSlotWeight0"], _C["kSlotWeight1"], _C["kSlotWeight2"]
+WEIGHTED_MIN_TILES = _C["kWeightedMinTiles"]
+BUCKETS = _C["kOrderBuckets"]
+
+
+def test_constants_come_from_the_device_header():
+    """Guards the parse: the weights the design describes (28 : 20 : 12, from 48 tiles a share),
+    16 length classes and shares of at least 16 tiles."""
+    assert (W0, W1, W2, WEIGHTED_MIN_TILES, BUCKETS, K_MIN_SHARE_TILES) == (28, 20, 12, 48, 16, 16)
 
 
 def balanced_groups(W, nw):
