@@ -443,11 +443,9 @@ def shared_blocks_flag(w, lib):
     return (lib.PA_DECODE_SHARED_BLOCKS if shared else 0), shared
 
 
-def time_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fused=False):
-    """Uploads ``args.replicas`` copies of the workload, runs ``args.warmup`` untimed steps, then
-    three passes of ``args.steps`` steps each: the timed pass (device-synchronised on both sides),
-    a pass with the library's HIP events around every launch (per-kernel averages), and a pass with
-    an event between steps (percentiles). Returns a dict of the measurements."""
+def prepare_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fused=False):
+    """Uploads ``args.replicas`` copies of the workload and its workspace; returns the step
+    function and what the timing needs (``time_steps``)."""
     from paged_kv_cache_318_amd.step import decode_step, decode_step_grouped, workspace_for
     from workloads.device import torch_dtype, upload
 
@@ -482,6 +480,22 @@ def time_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fused
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=partition,
                     variant=variant, workspace=ws, flags=flags, fused=fused)
 
+    G = w.num_heads // w.num_kv_heads
+    mfma_ok = w.dtype != "f32" and G <= 16
+    kernel = "decode_mfma" if (grouped or variant == 2 or (variant == 0 and mfma_ok and G >= 2)) \
+        else "decode_valu"
+    return {"w": w, "step": step, "buffers": [reps, out, ws, gr], "kernel": kernel, "shared": shared,
+            "grouped": None if gr is None else
+            {"groups": gr["groups"], "max_prefix_blocks": gr["max_prefix_blocks"]}}
+
+
+def time_steps(prep, args, lib, torch):
+    """Runs ``args.warmup`` untimed steps of a prepared workload, then three passes of
+    ``args.steps`` steps each: the timed pass (device-synchronised on both sides), a pass with the
+    library's HIP events around every launch (per-kernel averages), and a pass with an event
+    between steps (percentiles). Frees the workload's device buffers and returns the
+    measurements."""
+    w, step = prep["w"], prep["step"]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -525,16 +539,11 @@ def time_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fused
 
     print(f"[bench] {w.name}: timed {args.steps} steps, {ms_step * 1e3:.1f} us/step", file=sys.stderr,
           flush=True)
-    G = w.num_heads // w.num_kv_heads
-    mfma_ok = w.dtype != "f32" and G <= 16
-    kernel = "decode_mfma" if (grouped or variant == 2 or (variant == 0 and mfma_ok and G >= 2)) \
-        else "decode_valu"
-    del reps, out, ws
-    torch.cuda.empty_cache()
+    prep["buffers"].clear()
+    prep["step"] = None
     return {"ms_step": ms_step, "ms_step_profiled": ms_step_profiled, "kernels_ms": kern,
-            "pcts": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}, "kernel": kernel,
-            "shared": shared, "grouped": None if gr is None else
-            {"groups": gr["groups"], "max_prefix_blocks": gr["max_prefix_blocks"]}}
+            "pcts": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}, "kernel": prep["kernel"],
+            "shared": prep["shared"], "grouped": prep["grouped"]}
 
 
 def us(ms):
@@ -557,13 +566,24 @@ ALSO = (("cfg2-opt13b-mha-bf16", 2, {"dtype": "bf16"}, False, False),
         ("cfg4-shared-prefix-bf16-grouped", 4, {}, True, True))
 
 
-def measure_also(args, lib, torch, config):
-    res = {}
+def generate_also(config):
+    """The other workloads, generated on the host before any timing (so that no measurement
+    follows seconds of an idle GPU)."""
+    ws = []
     for label, n, over, grouped, unique in ALSO:
         t0 = time.perf_counter()
-        w = config(n, **over)
-        gen = time.perf_counter() - t0
-        m = time_steps(w, args, lib, torch, grouped=grouped)
+        ws.append(config(n, **over))
+        print(f"[bench] generated {label} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+    return ws
+
+
+def measure_also(args, lib, torch, preps):
+    """Times the prepared other workloads one after another (the GPU kept busy between them)."""
+    res = {}
+    for (label, n, over, grouped, unique), prep in zip(ALSO, preps):
+        w = prep["w"]
+        m = time_steps(prep, args, lib, torch)
         dec, achieved, frac = decode_roofline(w, m, unique)
         step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
         res[label] = {
@@ -580,8 +600,8 @@ def measure_also(args, lib, torch, config):
             "cache_dtype": w.dtype, "num_seqs": w.num_seqs, "attended_tokens": w.attended_tokens,
         }
         print(f"[bench] also {label}: attention kernel {res[label]['attention_kernel_us']} us, "
-              f"frac {res[label]['frac']} (generated in {gen:.1f}s)", file=sys.stderr, flush=True)
-        del w
+              f"frac {res[label]['frac']}", file=sys.stderr, flush=True)
+        prep["w"] = None
     return res
 
 
@@ -620,6 +640,9 @@ def main():
           f"{w.kv_bytes() / 1e9:.3f} GB K/V per call, generated in {t_gen:.1f}s", file=sys.stderr,
           flush=True)
 
+    do_also = not args.no_also and args.config == 2 and not over and not args.grouped
+    also_ws = generate_also(config) if do_also else []
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -630,8 +653,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     lib.load()
     calibration_copy(args, torch)
-    m = time_steps(w, args, lib, torch, grouped=args.grouped, variant=args.variant,
-                   partition=args.partition, fused=args.fused)
+    # every workload is on the device before the first timed step; the others are timed right
+    # after the headline one
+    prep = prepare_steps(w, args, lib, torch, grouped=args.grouped, variant=args.variant,
+                         partition=args.partition, fused=args.fused)
+    also_preps = [prepare_steps(x, args, lib, torch, grouped=g)
+                  for x, (_, _, _, g, _) in zip(also_ws, ALSO)]
+    del also_ws
+    m = time_steps(prep, args, lib, torch)
     ms_step = m["ms_step"]
     step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -683,9 +712,9 @@ def main():
         "cpu_baseline": None if cpu is None else cpu[0],
         "cpu_baseline_1t": None if cpu is None else cpu[1],
     }
-    del w
-    if not args.no_also and args.config == 2 and not over:
-        line["also"] = measure_also(args, lib, torch, config)
+    del w, prep
+    if also_preps:
+        line["also"] = measure_also(args, lib, torch, also_preps)
     if not args.no_ceiling:
         ceil = read_ceiling(lib, line["config"]["block_size"] * line["config"]["head_dim"] *
                             (1 if line["dtype"] == "fp8" else 2) * (2 if line["dtype"] == "f32" else 1))
