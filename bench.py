@@ -435,6 +435,17 @@ def measured_traffic(kernel: str, workload: str, summary: str = "decode_hbm_traf
     return None
 
 
+def blocks_shared_across_groups(w, group_start) -> bool:
+    """Whether some physical block is attended by sequences of two different groups."""
+    owner = {}
+    for gi in range(len(group_start) - 1):
+        for s in range(int(group_start[gi]), int(group_start[gi + 1])):
+            for b in w.tables[s, : -(-int(w.lens[s]) // w.block_size)].tolist():
+                if owner.setdefault(b, gi) != gi:
+                    return True
+    return False
+
+
 def shared_blocks_flag(w, lib):
     """PA_DECODE_SHARED_BLOCKS when the host's tables show sequences sharing physical blocks."""
     import numpy as np
@@ -462,6 +473,10 @@ def prepare_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fu
         G = w.num_heads // w.num_kv_heads
         mg = max(1, 16 // G)
         gs, pref = shared_prefix_groups(w.tables, w.lens, w.block_size, mg)
+        # the grouped kernel reads each group's shared blocks once: K/V are streamed unless a
+        # block is also shared between different groups
+        flags = lib.PA_DECODE_SHARED_BLOCKS if blocks_shared_across_groups(w, gs) else 0
+        shared = bool(flags)
         gws = torch.empty(lib.pa_decode_grouped_workspace_bytes(
             w.num_seqs, w.num_heads, w.head_dim, w.tables.shape[1], w.block_size, partition),
             dtype=torch.uint8, device="cuda")

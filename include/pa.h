@@ -223,6 +223,9 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  *   max_group_size host int: the largest group; max_group_size * (num_heads / num_kv_heads) <= 16
  *                  (each member's query heads become rows of the matrix-core tile).
  *   workspace      at least pa_decode_grouped_workspace_bytes(...) bytes (never NULL).
+ *   flags: PA_DECODE_SHARED_BLOCKS only when blocks are also shared between different groups;
+ *                  the kernel itself reads each group's shared blocks once, and streams them
+ *                  faster without the hint.
  *   everything else as for pa_decode; the cache must be 16-bit or fp8 (matrix-core kernel).
  */
 size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_heads, int head_dim,
