@@ -62,6 +62,18 @@ def test_shared_prefix_batch(flags):
     assert np.max(np.abs(got - run_gpu(w, out_dt="f32", flags=flags))) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("part", [0, 64])
+def test_grouped_load_hint_keeps_the_bits(part):
+    """Without PA_DECODE_SHARED_BLOCKS the grouped kernel reads K and V with streaming loads, with
+    it through the caches: a load hint only, so the two results agree bit for bit."""
+    w = share_prefixes(make_workload(LENS, num_heads=8, num_kv_heads=2, head_dim=128, dtype="fp8",
+                                     q_dtype="bf16", seed=17), 4)
+    a, _, pref = run_grouped(w, part=part, max_group_size=4)
+    b, _, _ = run_grouped(w, part=part, max_group_size=4, flags=lib.PA_DECODE_SHARED_BLOCKS)
+    assert pref.max() > 0
+    assert np.array_equal(a, b)
+
+
 COMBOS = [  # cache, q, Hq, Hkv, D, B, partition tokens, samples per group (rows = samples * G)
     ("bf16", "bf16", 8, 8, 128, 16, 0, 4),
     ("f16", "f16", 4, 2, 64, 8, 32, 4),
