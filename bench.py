@@ -47,6 +47,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-also", action="store_true",
                    help="skip the other decode workloads the headline run also measures")
+    p.add_argument("--also-warmup", type=int, default=50,
+                   help="untimed steps before each of the other workloads (at least --warmup): "
+                        "those lines report the kernels at the steady state of a decode loop")
     p.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of each leg of the oracle timing (all cores, one thread)")
@@ -596,9 +599,11 @@ def generate_also(config):
 def measure_also(args, lib, torch, preps):
     """Times the prepared other workloads one after another (the GPU kept busy between them)."""
     res = {}
+    also_args = argparse.Namespace(**vars(args))
+    also_args.warmup = max(args.warmup, args.also_warmup)
     for (label, n, over, grouped, unique), prep in zip(ALSO, preps):
         w = prep["w"]
-        m = time_steps(prep, args, lib, torch)
+        m = time_steps(prep, also_args, lib, torch)
         dec, achieved, frac = decode_roofline(w, m, unique)
         step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
         res[label] = {
@@ -730,6 +735,7 @@ def main():
     del w, prep
     if also_preps:
         line["also"] = measure_also(args, lib, torch, also_preps)
+        line["also_warmup"] = max(args.warmup, args.also_warmup)
     if not args.no_ceiling:
         ceil = read_ceiling(lib, line["config"]["block_size"] * line["config"]["head_dim"] *
                             (1 if line["dtype"] == "fp8" else 2) * (2 if line["dtype"] == "f32" else 1))
