@@ -195,6 +195,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   The array is shared by every call on one GPU and nothing in it needs clearing between calls
  *   (every partial result the merge reads is written by the same call). Calls that overlap on one
  *   GPU (on different streams, or from different threads without ordering) race on it.
+ *   The array used is the current HIP device's: `stream` must be NULL or a stream of that device
+ *   (another device's stream returns PA_ERR_INVALID_ARG).
  */
 #define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
 

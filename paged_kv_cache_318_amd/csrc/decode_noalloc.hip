@@ -53,6 +53,18 @@ extern "C" int pa_decode_noalloc(void* out, const void* q, const void* k_cache,
                                  pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
                                  const float* k_scale, const float* v_scale, int partition_tokens,
                                  int variant, int flags, void* stream) {
+  // the array used is the current device's: a stream of another device would have its kernels
+  // read and write that device's address on a different GPU
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    int cur = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess ||
+        hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return PA_ERR_INVALID_ARG;
+    }
+    if (sdev != cur) return PA_ERR_INVALID_ARG;
+  }
   return pa::decode_with_library_workspace(
       out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
       head_dim, block_size, max_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, out_dtype,
