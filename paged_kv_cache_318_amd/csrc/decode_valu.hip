@@ -35,9 +35,10 @@ constexpr int kValuBlocksPerIter = 2;
 
 // NT: read K/V tiles non-temporally (streaming; the default) or through the caches (when blocks
 // are shared between sequences of the batch and a tile fetched for one is reused by another).
-// Grid (query head, sequence, partition), or with a.ordered a 1-D grid of (item, query head),
-// query head fastest, over the ordered work list (longest work first; see pa_sched.h), the lengths
-// staged in dynamic LDS.
+// Grid (query head, sequence, partition), or with a.ordered a 1-D grid over the ordered work list
+// (longest work first), its (item, query head) pairs, query head fastest, handed out with the
+// odd-numbered XCDs taking 8 for every 9 the even ones take (pa_sched.h); the lengths staged in
+// dynamic LDS.
 template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = Elem<CDT>::bytes;
@@ -52,8 +53,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   int h, s, p, L;
   if (a.ordered) {
     extern __shared__ int order_lds[];
-    h = static_cast<int>(blockIdx.x % Hq);
-    const int2 it = ordered_item(a, B, blockIdx.x / Hq, order_lds);
+    const long long unit = xcd_weighted_item(blockIdx.x);
+    if (unit < 0) return;  // an odd-numbered XCD's empty work-group
+    h = static_cast<int>(unit % Hq);
+    const int2 it = ordered_item(a, B, unit / Hq, order_lds);
     if (it.x < 0) return;
     s = __builtin_amdgcn_readfirstlane(it.x);
     p = __builtin_amdgcn_readfirstlane(it.y);
@@ -395,7 +398,8 @@ static hipError_t launch_valu_d(const DecodeArgs& a, int D, int B, dim3 grid, hi
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int cdt, int qdt, int D, int B, hipStream_t st) {
-  const dim3 grid = a.ordered ? dim3(a.num_heads * a.num_seqs * a.max_parts)
+  const dim3 grid = a.ordered ? dim3(static_cast<unsigned>(xcd_weighted_grid(
+                                    static_cast<long long>(a.num_heads) * a.num_seqs * a.max_parts)))
                               : dim3(a.num_heads, a.num_seqs, a.max_parts);
   if (cdt == DT_F32 && qdt == DT_F32) return launch_valu_d<DT_F32, DT_F32>(a, D, B, grid, st);
   if (cdt == DT_F16 && qdt == DT_F16) return launch_valu_d<DT_F16, DT_F16>(a, D, B, grid, st);

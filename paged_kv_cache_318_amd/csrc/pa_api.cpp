@@ -476,7 +476,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // (the ordered list's 1-D grid must also fit, else the 3-D grid takes the batch; the
   // ordering's length classes multiply a partition's block count by 16 in 32 bits)
   a.ordered = (order_ok && stream_kv && static_cast<int64_t>(pl.part_blocks) * block_size >= kMinOrderedPartition &&
-               pl.part_blocks <= (1 << 26) && units * pl.max_parts <= kMaxGridX) ? 1 : 0;
+               pl.part_blocks <= (1 << 26) && pa::xcd_weighted_grid(units * pl.max_parts) <= kMaxGridX) ? 1 : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_slots = k_new != nullptr ? slot_mapping : nullptr;

@@ -237,6 +237,44 @@ __device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int
   return make_int2(s, ((lens_l[s] + B - 1) / B) / pb);
 }
 
+// ---- the ordered list's items over the XCDs --------------------------------------------------
+//
+// Work-groups go to the 8 XCDs round-robin by index (work-group w to XCD w mod 8), and each XCD
+// dispatches its own in index order. On the MHA decode batch (64 sequences, 40 heads, one item
+// per (sequence, head)) the odd-numbered XCDs took 8-13% longer per work-group than the even ones
+// for the same items, so with an even split the even XCDs ran out of work 15-20 us before the odd
+// ones. The VALU kernel's ordered grid therefore hands the list out in periods of kXcdRounds
+// rounds of 8 work-groups, and in the last round of each period the odd-numbered XCDs get an
+// empty work-group (it exits at once): they take 8 items for every 9 the even ones take. That
+// kernel took 241.4-242.0 us against 246.3-247.0 us for the plain order, its XCDs' mean
+// work-group times evened out (59-63 us on every XCD), and the same rounds with the even XCDs
+// sitting out took 248.6-249.0 us. Periods of 7 rounds measured the same as 9; 5, 6, 13 and 25
+// gained less. (On the GQA batch's MFMA grid the same order measured within 1 us of the plain
+// one, so that grid keeps it.) Which work-group takes an item never changes the item's result.
+
+constexpr int kXcdRounds = 9;
+
+// Items one period of kXcdRounds rounds hands out: 8 per round, 4 in the last.
+__host__ __device__ constexpr long long xcd_items_per_period() { return 8LL * kXcdRounds - 4; }
+
+// Work-groups of the grid that hands out `items` items (whole periods).
+__host__ __device__ constexpr long long xcd_weighted_grid(long long items) {
+  return (items + xcd_items_per_period() - 1) / xcd_items_per_period() * 8 * kXcdRounds;
+}
+
+// The item of the list work-group w takes, or -1 for an odd-numbered XCD's empty work-group.
+__device__ __forceinline__ long long xcd_weighted_item(long long w) {
+  const int x = static_cast<int>(w & 7);
+  const long long r = w >> 3;
+  const int rr = static_cast<int>(r % kXcdRounds);
+  const long long per = r / kXcdRounds;
+  if (rr == kXcdRounds - 1) {
+    if (x & 1) return -1;
+    return per * xcd_items_per_period() + 8LL * (kXcdRounds - 1) + (x >> 1);
+  }
+  return per * xcd_items_per_period() + 8LL * rr + x;
+}
+
 // The sequence holding tile t (t < pref[S] * hu): the largest s with pref[s] * hu <= t, which is
 // never an empty sequence.
 __device__ __forceinline__ int find_seq(const int* pref, int S, long long hu, long long t) {

@@ -9,7 +9,10 @@ arithmetic that decides which work-group reads which tiles, on many shapes at no
   unit -- names the share that holds every tile;
 * ordered fixed partitions -- the ordered list holds every (sequence, partition) item exactly once
   plus one item per empty sequence, full partitions first, then last partitions longest class
-  first, and the grid covers it.
+  first, and the grid covers it;
+* the XCD-weighted order of that list (VALU kernel) -- every item goes to exactly one work-group,
+  the odd-numbered XCDs (work-group index odd) take 8 items for every 9 the even ones take, and
+  only their work-groups are ever empty.
 """
 
 import os
@@ -38,12 +41,14 @@ K_MIN_SHARE_TILES = _C["kMinShareTiles"]
 W0, W1, W2 = _C["kSlotWeight0"], _C["kSlotWeight1"], _C["kSlotWeight2"]
 WEIGHTED_MIN_TILES = _C["kWeightedMinTiles"]
 BUCKETS = _C["kOrderBuckets"]
+XCD_ROUNDS = _C["kXcdRounds"]
 
 
 def test_constants_come_from_the_device_header():
     """Guards the parse: the weights the design describes (28 : 20 : 12, from 48 tiles a share),
-    16 length classes and shares of at least 16 tiles."""
-    assert (W0, W1, W2, WEIGHTED_MIN_TILES, BUCKETS, K_MIN_SHARE_TILES) == (28, 20, 12, 48, 16, 16)
+    16 length classes, shares of at least 16 tiles and periods of 9 rounds over the XCDs."""
+    assert (W0, W1, W2, WEIGHTED_MIN_TILES, BUCKETS, K_MIN_SHARE_TILES, XCD_ROUNDS) == \
+        (28, 20, 12, 48, 16, 16, 9)
 
 
 def balanced_groups(W, nw):
@@ -144,3 +149,43 @@ def test_ordered_list_holds_every_item_once(pb):
         tail = sizes[nf:]
         cls = [BUCKETS - 1 if x == 0 else (pb - x) * BUCKETS // pb for x in tail]
         assert cls == sorted(cls)
+
+
+def xcd_items_per_period():
+    return 8 * XCD_ROUNDS - 4
+
+
+def xcd_weighted_grid(items):
+    return -(-items // xcd_items_per_period()) * 8 * XCD_ROUNDS
+
+
+def xcd_weighted_item(w):
+    x, r = w % 8, w // 8
+    rr, per = r % XCD_ROUNDS, r // XCD_ROUNDS
+    if rr == XCD_ROUNDS - 1:
+        return -1 if x % 2 else per * xcd_items_per_period() + 8 * (XCD_ROUNDS - 1) + x // 2
+    return per * xcd_items_per_period() + 8 * rr + x
+
+
+@pytest.mark.parametrize("items", [1, 7, 67, 68, 69, 136, 2560, 10007, 123457])
+def test_xcd_weighted_order_hands_out_every_item_once(items):
+    grid = xcd_weighted_grid(items)
+    taken = [xcd_weighted_item(w) for w in range(grid)]
+    real = [i for i in taken if i >= 0]
+    assert len(real) == len(set(real))                      # no item twice
+    assert set(range(items)) <= set(real)                   # every item of the list
+    assert len(real) == grid // (8 * XCD_ROUNDS) * xcd_items_per_period()
+    assert grid - 8 * XCD_ROUNDS < items * 8 * XCD_ROUNDS / xcd_items_per_period() <= grid
+    per_xcd = [0] * 8
+    for w, i in enumerate(taken):
+        if i < 0:                                           # empty: an odd XCD, a period's last round
+            assert w % 2 == 1 and (w // 8) % XCD_ROUNDS == XCD_ROUNDS - 1
+        else:
+            per_xcd[w % 8] += 1
+    periods = grid // (8 * XCD_ROUNDS)
+    assert per_xcd == [XCD_ROUNDS * periods if x % 2 == 0 else (XCD_ROUNDS - 1) * periods
+                       for x in range(8)]
+    # within an XCD the items keep the list's order (each XCD dispatches by index)
+    for x in range(8):
+        mine = [i for w, i in enumerate(taken) if w % 8 == x and i >= 0]
+        assert mine == sorted(mine)
