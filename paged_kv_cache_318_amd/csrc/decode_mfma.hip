@@ -28,7 +28,9 @@
 //     4-byte (fp8) load, and one load instruction covers 16 whole dim rows of the tile.
 //   * keys are staged through LDS with gfx950's direct global -> LDS loads: every load
 //     instruction reads 1 KB of the tile contiguously (whole cache lines, non-temporal) and the
-//     MFMA-layout reads come back out of an XOR-swizzled LDS copy.
+//     MFMA-layout reads come back out of an XOR-swizzled LDS copy. fp8 caches with 16-token
+//     blocks stage the value tiles the same way (as stored) and issue each iteration's loads
+//     while the iteration before it computes.
 // The weights P are fed to the MFMA as a 16-bit hi part plus a 16-bit remainder (two MFMAs), so
 // they carry ~16 significant bits instead of 8 (bf16) or 11 (fp16).
 // fp8 caches: codes are converted exactly to the MFMA input type; the per-(block, kv head) key
@@ -47,13 +49,21 @@ namespace pa {
 constexpr int kFp8BlocksPerIter = 2;
 constexpr int mfma_blocks_per_iter(int elem_bytes) { return elem_bytes == 2 ? 2 : kFp8BlocksPerIter; }
 
-// Bytes of dynamic LDS: the staged key tiles of one iteration per wave (reused by the merge of
-// the four waves at the end of a segment) plus, for the balanced split and the ordered fixed
-// partitions, the batch's lengths and prefix sums.
-template <int CDT, int D>
+// fp8 caches with 16-token blocks stage the value tiles through LDS too (next to the keys), so
+// that every K/V load of the segment loop is a direct-to-LDS load and the loop can issue each
+// iteration's loads one step ahead (fp8 batch: 134.7-135.1 -> 129.7-130.1 us). With register loads
+// in flight beside direct-to-LDS loads the compiler drains every load before the first read of a
+// staged tile, which is why the values go through LDS too. At 16 bits the second stage would
+// leave two work-groups per CU.
+constexpr bool mfma_stages_values(int cdt, int block_size) { return cdt == DT_FP8 && block_size == 16; }
+
+// Bytes of dynamic LDS: the staged key (and staged value) tiles of one iteration per wave (reused
+// by the merge of the four waves at the end of a segment) plus, for the balanced split and the
+// ordered fixed partitions, the batch's lengths and prefix sums.
+template <int CDT, int D, int B>
 constexpr size_t mfma_lds_bytes(int G, int S, bool sched_lds) {
-  const size_t stage =
-      size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes;
+  const size_t stage = size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes *
+                       (mfma_stages_values(CDT, B) ? 2 : 1);
   const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
   const size_t sched = sched_lds ? static_cast<size_t>(ordered_lds_ints(S)) * sizeof(int) : 0;
   return (stage > merge ? stage : merge) + sched;
@@ -92,6 +102,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   static_assert(BPI >= 1 && NBI % SUB == 0, "an iteration takes whole work items");
   constexpr int kKeyAux = NT ? 2 : 0;        // cache policy of the key loads (2: non-temporal)
   constexpr bool kNtV = NT;
+  constexpr bool kStageValues = mfma_stages_values(CDT, B);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, n = lane & 15;
@@ -132,7 +143,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // (l % CPR) ^ (row % CPR) of its row, so LDS holds each row XOR-swizzled by its index and the
   // score-operand reads below (16 rows at one chunk column) fall into distinct banks. PAIR: rows
   // 0-7 come from the first block, 8-15 from the second (dsec: this lane's row is in the second).
-  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT);
+  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT * (kStageValues ? 2 : 1));
+  [[maybe_unused]] uint8_t* vbuf = kbuf + NBI * KT;  // the staged value tiles (kStageValues)
   int dsrc[NI];
   bool dsec[NI];
 #pragma unroll
@@ -158,17 +170,263 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // 16-token part u % SUB of item u / SUB); their table entries are fetched CHUNK items at a time
   // into one VGPR (lane GB*j + h: block h of item j) and read back with readlane
   const int nmine = wave < nitems ? (nitems - wave + 3) / 4 : 0;
+
+  // ---- the math of one iteration, shared by both loops below ----
+  // scores of the iteration's tiles from the staged keys
+  auto tile_scores = [&](int nlive, f32x4 (&zt)[NBI]) {
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {
+      zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u / SUB >= nlive) continue;
+      const uint8_t* kb = kbuf + u * KT;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
+        if constexpr (EB == 2) {
+          zt[u] = mfma_k32<QDT>(raw, qop[i], zt[u]);
+        } else {
+          const u32x4 k0{fp8x2_to16<QDT, false>(raw.x), fp8x2_to16<QDT, true>(raw.x),
+                         fp8x2_to16<QDT, false>(raw.y), fp8x2_to16<QDT, true>(raw.y)};
+          zt[u] = mfma_k32<QDT>(k0, qop[2 * i], zt[u]);
+          const u32x4 k1{fp8x2_to16<QDT, false>(raw.z), fp8x2_to16<QDT, true>(raw.z),
+                         fp8x2_to16<QDT, false>(raw.w), fp8x2_to16<QDT, true>(raw.w)};
+          zt[u] = mfma_k32<QDT>(k1, qop[2 * i + 1], zt[u]);
+        }
+      }
+    }
+  };
+  // the online softmax over the iteration's scores: the weights pz, the running max and sum, the
+  // accumulator rescaled; valid[u] = this lane group's tokens of tile u below lim (<= 0: none)
+  auto online_softmax = [&](int ia, int nlive, const f32x4 (&zt)[NBI], const float (&zs_l)[NBI],
+                            int (&valid)[NBI], float (&pz)[4 * NBI]) {
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+      valid[u] = u / SUB < nlive ? lim - tile_start(ia + 4 * (u / SUB), u) - 4 * q4 : 0;
+    float z[4 * NBI];
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[4 * u + i] = (i < valid[u]) ? zt[u][i] * zs_l[u] : neg_inf();
+    float tm = z[0];
+#pragma unroll
+    for (int i = 1; i < 4 * NBI; ++i) tm = fmaxf(tm, z[i]);
+    tm = pair32_max(pair16_max(tm));
+    const float mn = fmaxf(m, tm);  // finite: the iteration's first item starts below lim
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4 * NBI; ++i) {
+      pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
+      psum += pz[i];
+    }
+    lsum = lsum * alpha + psum;
+    m = mn;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
+  };
+  // weighted values, two tiles (32 tokens) per MFMA: k 0..3 are tokens 4*q4.. of the pair's
+  // first tile, k 4..7 those of its second; P^T goes in as a 16-bit hi part and remainder.
+  // Tokens at or beyond L get zero values (their weights are already 0).
+  auto weighted_values = [&](int nlive, const Raw<4 * EB> (&vr)[NBI][MI], const float (&vs_l)[NBI],
+                             const float (&pz)[4 * NBI], const int (&valid)[NBI]) {
+#pragma unroll
+    for (int pr = 0; pr < NBI / 2; ++pr) {
+      if ((2 * pr) / SUB >= nlive) break;
+      const int u0 = 2 * pr, u1 = 2 * pr + 1;
+      // (gfx950's packed converters, round to nearest even: two weights an instruction)
+      uint32_t phw[4], plw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = i < 2 ? vs_l[u0] : vs_l[u1];
+        const float p0 = pz[4 * u0 + 2 * i] * sc, p1 = pz[4 * u0 + 2 * i + 1] * sc;
+        split16x2<QDT>(p0, p1, phw[i], plw[i]);
+      }
+      const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
+      const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};
+      const uint32_t ma0 = valid[u0] >= 2 ? 0xffffffffu : (valid[u0] == 1 ? 0x0000ffffu : 0u);
+      const uint32_t ma1 = valid[u0] >= 4 ? 0xffffffffu : (valid[u0] == 3 ? 0x0000ffffu : 0u);
+      const uint32_t mb0 = valid[u1] >= 2 ? 0xffffffffu : (valid[u1] == 1 ? 0x0000ffffu : 0u);
+      const uint32_t mb1 = valid[u1] >= 4 ? 0xffffffffu : (valid[u1] == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        uint32_t a0, a1, c0, c1;
+        if constexpr (EB == 2) {
+          a0 = vr[u0][mi].w[0];
+          a1 = vr[u0][mi].w[1];
+          c0 = vr[u1][mi].w[0];
+          c1 = vr[u1][mi].w[1];
+        } else {
+          a0 = fp8x2_to16<QDT, false>(vr[u0][mi].w[0]);
+          a1 = fp8x2_to16<QDT, true>(vr[u0][mi].w[0]);
+          c0 = fp8x2_to16<QDT, false>(vr[u1][mi].w[0]);
+          c1 = fp8x2_to16<QDT, true>(vr[u1][mi].w[0]);
+        }
+        const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
+        acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
+        acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
+      }
+    }
+  };
+  // the table entries of chunk base_i (cnt items) of this wave
+  auto chunk_table = [&](int base_i, int cnt) {
+    int tv = 0;
+    if (lane < cnt * GB) {
+      // a pair's second block past the segment's end stands in as its first block: its tokens are
+      // masked, but its scales multiply zero weights, so they must be those of a block in use (a
+      // free block's may be anything, NaN included)
+      const int blk = b0 + GB * (wave + 4 * (base_i + lane / GB)) + lane % GB;
+      tv = trow[blk < b1 ? blk : blk - 1];
+      tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
+    }
+    return tv;
+  };
+
+  if constexpr (kStageValues) {
+  // ---- fp8 keys and values both staged through LDS, each iteration's loads issued one step
+  // ahead: the next iteration's keys once this one's scores have read the key slots, its values
+  // once this one's value operands are in registers. Every K/V load of the loop is then a
+  // direct-to-LDS load whose completion the explicit counts below track; the table entries and
+  // the query operands (register loads) are waited for before the first of them. ----
+  typedef __attribute__((address_space(4))) const float cfloat_t;  // (scalar loads of the scales)
+  constexpr int NVI = KT / 1024;  // value load instructions per tile
+  // vmcnt(N) lgkmcnt(0): every direct load but the last N issued, and every LDS access
+  constexpr int kWaitKeys = ((NBI * NVI) & 15) | (7 << 4) | (((NBI * NVI) >> 4) << 14);
+  constexpr int kWaitValues = ((NBI * NI) & 15) | (7 << 4) | (((NBI * NI) >> 4) << 14);
+  constexpr int kWaitLds = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0), no vmcnt wait
+  static_assert(NBI * NVI <= 63 && NBI * NI <= 63, "vmcnt field");
   for (int base_i = 0; base_i < nmine; base_i += CHUNK) {
   const int cnt = min(CHUNK, nmine - base_i);
-  int tv = 0;
-  if (lane < cnt * GB) {
-    // a pair's second block past the segment's end stands in as its first block: its tokens are
-    // masked, but its scales multiply zero weights, so they must be those of a block in use (a
-    // free block's may be anything, NaN included)
-    const int blk = b0 + GB * (wave + 4 * (base_i + lane / GB)) + lane % GB;
-    tv = trow[blk < b1 ? blk : blk - 1];
-    tv = tv < 0 ? 0 : (tv >= a.num_blocks ? a.num_blocks - 1 : tv);
+  const int tv = chunk_table(base_i, cnt);
+  __builtin_amdgcn_s_waitcnt(0);
+  auto tiles_at = [&](int it, int nl, int (&pb)[NBI], size_t (&tb)[NBI]) {
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {
+      pb[u] = __builtin_amdgcn_readlane(tv, it + (u < nl ? u : 0));
+      tb[u] = (static_cast<size_t>(pb[u]) * Hkv + g) * KTB;
+    }
+  };
+  auto issue_keys = [&](int nl, const size_t (&tb)[NBI]) {
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+      if (u < nl) {
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + tb[u] + dsrc[ii], kbuf + u * KT + 1024 * ii);
+      }
+  };
+  auto issue_values = [&](int nl, const size_t (&tb)[NBI]) {  // [D][16] codes as stored, 1 KB a load
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+      if (u < nl) {
+#pragma unroll
+        for (int ii = 0; ii < NVI; ++ii)
+          dma16<kKeyAux>(a.v_cache + tb[u] + 1024 * ii + 16 * lane, vbuf + u * KT + 1024 * ii);
+      }
+  };
+  auto scales_of = [&](const int (&pb)[NBI], float (&zs)[NBI], float (&vs)[NBI]) {
+#pragma unroll
+    for (int u = 0; u < NBI; ++u) {
+      const size_t ix = static_cast<size_t>(pb[u]) * Hkv + g;
+      zs[u] = a.zscale * ((cfloat_t*)a.k_scale)[ix];
+      vs[u] = ((cfloat_t*)a.v_scale)[ix];
+    }
+  };
+  size_t ba[NBI];
+  float zs_l[NBI], vs_l[NBI];
+  {
+    const int nl = min(BPI, cnt);
+    int pba[NBI];
+    tiles_at(0, nl, pba, ba);
+    issue_keys(nl, ba);
+    issue_values(nl, ba);
+    scales_of(pba, zs_l, vs_l);
   }
+  for (int it = 0; it < cnt; it += BPI) {
+    const int nlive = min(BPI, cnt - it);
+    const int ia = wave + 4 * (base_i + it);
+    const int nl_next = it + BPI < cnt ? min(BPI, cnt - it - BPI) : 0;
+    int u_new = -1;
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+      if (slot_new >= 0 && u < nlive && ia + 4 * u == item_new) u_new = u;
+    // this iteration's keys have landed (its values, issued after them, may still be in flight)
+    if (u_new < 0 && nlive == BPI) __builtin_amdgcn_s_waitcnt(kWaitKeys);
+    else __builtin_amdgcn_s_waitcnt(0);
+    if (u_new >= 0) {  // the new token's key row into the staged tile and into the cache
+      const size_t pbn = static_cast<size_t>(slot_new / B);
+      const float ks = a.k_scale[pbn * Hkv + g];
+      if (lane < D / 8) {
+        const u32x4 kn = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint16_t*>(a.k_new) + (static_cast<size_t>(s) * Hkv + g) * D + 8 * lane);
+        Raw<16> in;
+        in.w[0] = kn.x; in.w[1] = kn.y; in.w[2] = kn.z; in.w[3] = kn.w;
+        const Raw<8> kc = new_key_piece<CDT, QDT, 8>(in, ks);
+        store_raw<8>(kbuf + u_new * KT + o_new * CPR * 16 + 16 * ((lane / 2) ^ (o_new % CPR)) + 8 * (lane % 2), kc);
+        store_raw<8>(const_cast<uint8_t*>(a.k_cache) + (pbn * Hkv + g) * KTB + (slot_new % B) * D + 8 * lane, kc);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    f32x4 zt[NBI];
+    tile_scores(nlive, zt);
+    // the key slots are read: the next iteration's keys
+    int pba_n[NBI];
+    size_t ba_n[NBI];
+    float zs_n[NBI], vs_n[NBI];
+    if (nl_next > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitLds);
+      tiles_at(it + BPI, nl_next, pba_n, ba_n);
+      issue_keys(nl_next, ba_n);
+      scales_of(pba_n, zs_n, vs_n);
+    }
+    int valid[NBI];
+    float pz[4 * NBI];
+    online_softmax(ia, nlive, zt, zs_l, valid, pz);
+    // this iteration's values have landed (the next keys, issued after them, may still be in flight)
+    if (u_new < 0 && nl_next == BPI) __builtin_amdgcn_s_waitcnt(kWaitValues);
+    else __builtin_amdgcn_s_waitcnt(0);
+    Raw<4> vr[NBI][MI];  // lane (q4, n): dim row 16*mi + n, tokens 4*q4 .. 4*q4+3 of tile u
+#pragma unroll
+    for (int u = 0; u < NBI; ++u)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        vr[u][mi].w[0] = *reinterpret_cast<const uint32_t*>(vbuf + u * KT + (16 * mi + n) * 16 + 4 * q4);
+    if (u_new >= 0) {  // the new token's value codes into the operands and the block's rows back
+      const size_t pbn = static_cast<size_t>(slot_new / B);
+      const float vsn = a.v_scale[pbn * Hkv + g];
+      const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new) + (static_cast<size_t>(s) * Hkv + g) * D;
+#pragma unroll
+      for (int u = 0; u < NBI; ++u) {  // (u == u_new: a static index keeps vr in registers)
+        if (u != u_new) continue;
+        if (o_new >= 4 * q4 && o_new < 4 * q4 + 4) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+            put_elem<EB>(vr[u][mi], o_new - 4 * q4, new_value_bits<CDT, QDT>(vn[16 * mi + n], vsn));
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          store_raw<4>(const_cast<uint8_t*>(a.v_cache) + ba[u] + (16 * mi + n) * 16 + 4 * q4, vr[u][mi]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    // the value slots are read: the next iteration's values
+    if (nl_next > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitLds);
+      issue_values(nl_next, ba_n);
+    }
+    weighted_values(nlive, vr, vs_l, pz, valid);
+    if (nl_next > 0) {
+#pragma unroll
+      for (int u = 0; u < NBI; ++u) {
+        ba[u] = ba_n[u];
+        zs_l[u] = zs_n[u];
+        vs_l[u] = vs_n[u];
+      }
+    }
+  }
+  }
+  } else {
+  for (int base_i = 0; base_i < nmine; base_i += CHUNK) {
+  const int cnt = min(CHUNK, nmine - base_i);
+  const int tv = chunk_table(base_i, cnt);
   for (int it = 0; it < cnt; it += BPI) {
     const int nlive = min(BPI, cnt - it);  // work items of this iteration (the last may have fewer)
     const int ia = wave + 4 * (base_i + it);  // the iteration's first work item
@@ -287,93 +545,12 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
     // scores of the iteration's tiles
     f32x4 zt[NBI];
-#pragma unroll
-    for (int u = 0; u < NBI; ++u) {
-      zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u / SUB >= nlive) continue;
-      const uint8_t* kb = kbuf + u * KT;
-#pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
-        if constexpr (EB == 2) {
-          zt[u] = mfma_k32<QDT>(raw, qop[i], zt[u]);
-        } else {
-          const u32x4 k0{fp8x2_to16<QDT, false>(raw.x), fp8x2_to16<QDT, true>(raw.x),
-                         fp8x2_to16<QDT, false>(raw.y), fp8x2_to16<QDT, true>(raw.y)};
-          zt[u] = mfma_k32<QDT>(k0, qop[2 * i], zt[u]);
-          const u32x4 k1{fp8x2_to16<QDT, false>(raw.z), fp8x2_to16<QDT, true>(raw.z),
-                         fp8x2_to16<QDT, false>(raw.w), fp8x2_to16<QDT, true>(raw.w)};
-          zt[u] = mfma_k32<QDT>(k1, qop[2 * i + 1], zt[u]);
-        }
-      }
-    }
-    int valid[NBI];  // this lane group's tokens of the tile below lim (<= 0: none)
-#pragma unroll
-    for (int u = 0; u < NBI; ++u)
-      valid[u] = u / SUB < nlive ? lim - tile_start(ia + 4 * (u / SUB), u) - 4 * q4 : 0;
-    float z[4 * NBI];
-#pragma unroll
-    for (int u = 0; u < NBI; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[4 * u + i] = (i < valid[u]) ? zt[u][i] * zs_l[u] : neg_inf();
-    float tm = z[0];
-#pragma unroll
-    for (int i = 1; i < 4 * NBI; ++i) tm = fmaxf(tm, z[i]);
-    tm = pair32_max(pair16_max(tm));
-    const float mn = fmaxf(m, tm);  // finite: the iteration's first item starts below lim
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    tile_scores(nlive, zt);
+    int valid[NBI];
     float pz[4 * NBI];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4 * NBI; ++i) {
-      pz[i] = __builtin_amdgcn_exp2f(z[i] - mn);
-      psum += pz[i];
-    }
-    lsum = lsum * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) acc[mi] = acc[mi] * alpha;
-
-    // weighted values, two tiles (32 tokens) per MFMA: k 0..3 are tokens 4*q4.. of the pair's
-    // first tile, k 4..7 those of its second; P^T goes in as a 16-bit hi part and remainder.
-    // Tokens at or beyond L get zero values (their weights are already 0).
-#pragma unroll
-    for (int pr = 0; pr < NBI / 2; ++pr) {
-      if ((2 * pr) / SUB >= nlive) break;
-      const int u0 = 2 * pr, u1 = 2 * pr + 1;
-      // (gfx950's packed converters, round to nearest even: two weights an instruction)
-      uint32_t phw[4], plw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = i < 2 ? vs_l[u0] : vs_l[u1];
-        const float p0 = pz[4 * u0 + 2 * i] * sc, p1 = pz[4 * u0 + 2 * i + 1] * sc;
-        split16x2<QDT>(p0, p1, phw[i], plw[i]);
-      }
-      const u32x4 phi{phw[0], phw[1], phw[2], phw[3]};
-      const u32x4 plo{plw[0], plw[1], plw[2], plw[3]};
-      const uint32_t ma0 = valid[u0] >= 2 ? 0xffffffffu : (valid[u0] == 1 ? 0x0000ffffu : 0u);
-      const uint32_t ma1 = valid[u0] >= 4 ? 0xffffffffu : (valid[u0] == 3 ? 0x0000ffffu : 0u);
-      const uint32_t mb0 = valid[u1] >= 2 ? 0xffffffffu : (valid[u1] == 1 ? 0x0000ffffu : 0u);
-      const uint32_t mb1 = valid[u1] >= 4 ? 0xffffffffu : (valid[u1] == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        uint32_t a0, a1, c0, c1;
-        if constexpr (EB == 2) {
-          a0 = vr[u0][mi].w[0];
-          a1 = vr[u0][mi].w[1];
-          c0 = vr[u1][mi].w[0];
-          c1 = vr[u1][mi].w[1];
-        } else {
-          a0 = fp8x2_to16<QDT, false>(vr[u0][mi].w[0]);
-          a1 = fp8x2_to16<QDT, true>(vr[u0][mi].w[0]);
-          c0 = fp8x2_to16<QDT, false>(vr[u1][mi].w[0]);
-          c1 = fp8x2_to16<QDT, true>(vr[u1][mi].w[0]);
-        }
-        const u32x4 vop{a0 & ma0, a1 & ma1, c0 & mb0, c1 & mb1};
-        acc[mi] = mfma_k32<QDT>(vop, phi, acc[mi]);
-        acc[mi] = mfma_k32<QDT>(vop, plo, acc[mi]);
-      }
-    }
+    online_softmax(ia, nlive, zt, zs_l, valid, pz);
+    weighted_values(nlive, vr, vs_l, pz, valid);
+  }
   }
   }
   lds_barrier();  // every wave is done with its staged key tiles: the LDS is reused below
@@ -437,7 +614,7 @@ __global__ __launch_bounds__(256, 3) void decode_mfma_kernel(DecodeArgs a) {
   int g, s, p, L;
   if (a.ordered) {
     int* lds = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) +
-                                      mfma_lds_bytes<CDT, D>(G, 0, false));
+                                      mfma_lds_bytes<CDT, D, B>(G, 0, false));
     g = static_cast<int>(blockIdx.x % a.num_kv_heads);
     const int2 it = ordered_item(a, B, blockIdx.x / a.num_kv_heads, lds);
     if (it.x < 0) return;
@@ -472,7 +649,7 @@ template <int CDT, int QDT, int D, int B, bool NT>
 __global__ __launch_bounds__(256, 3) void decode_mfma_balanced_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   constexpr int EB = Elem<CDT>::bytes;
-  const size_t stage = mfma_lds_bytes<CDT, D>(a.num_heads / a.num_kv_heads, 0, false);
+  const size_t stage = mfma_lds_bytes<CDT, D, B>(a.num_heads / a.num_kv_heads, 0, false);
   int* lens_lds = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(smem) + stage);
   int* pref = lens_lds + a.num_seqs;
   scan_batch(a, B, lens_lds, pref);
@@ -548,12 +725,12 @@ static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
     // a.max_parts counts a sequence's prefix and own parts together (its slot stride); either kind
     // alone has at most a.max_parts - 1 parts, so the grid's part dimension stops there
     const dim3 grid(a.num_kv_heads, a.num_groups + a.num_seqs, a.max_parts - 1 > 0 ? a.max_parts - 1 : 1);
-    const size_t shm = mfma_lds_bytes<CDT, D>(16, 0, false);  // up to 16 rows
+    const size_t shm = mfma_lds_bytes<CDT, D, B>(16, 0, false);  // up to 16 rows
     if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
     else hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
     return hipGetLastError();
   }
-  const size_t shm = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.balanced != 0);
+  const size_t shm = mfma_lds_bytes<CDT, D, B>(G, a.num_seqs, a.balanced != 0);
   if (a.balanced) {
     const dim3 grid(a.nw);
     if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
@@ -561,7 +738,7 @@ static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
   } else {
     const dim3 grid = a.ordered ? dim3(a.num_kv_heads * a.num_seqs * a.max_parts)
                                 : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
-    const size_t shm_f = mfma_lds_bytes<CDT, D>(G, a.num_seqs, a.ordered != 0);
+    const size_t shm_f = mfma_lds_bytes<CDT, D, B>(G, a.num_seqs, a.ordered != 0);
     if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm_f, st, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm_f, st, a);
   }
@@ -592,10 +769,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int cdt, int qdt, int D, int 
 // never depends on the PA_DECODE_SHARED_BLOCKS hint.
 int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S) {
   const void* k[2] = {nullptr, nullptr};
+  size_t shm = 0;
 #define PA_PICK(C, Q, DD, BB)                                                              \
   if (cdt == C && qdt == Q && D == DD && B == BB) {                                        \
     k[0] = reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, true>);  \
     k[1] = reinterpret_cast<const void*>(&decode_mfma_balanced_kernel<C, Q, DD, BB, false>); \
+    shm = mfma_lds_bytes<C, DD, BB>(G, S, true);                                           \
   }
 #define PA_PICK_B(C, Q, DD) PA_PICK(C, Q, DD, 8) PA_PICK(C, Q, DD, 16) PA_PICK(C, Q, DD, 32)
   PA_PICK_B(DT_F16, DT_F16, 64) PA_PICK_B(DT_F16, DT_F16, 128) PA_PICK_B(DT_BF16, DT_BF16, 64)
@@ -604,9 +783,6 @@ int mfma_groups_per_cu(int cdt, int qdt, int D, int B, int G, int S) {
 #undef PA_PICK_B
 #undef PA_PICK
   if (k[0] == nullptr) return 0;
-  size_t shm = 0;
-  if (cdt == DT_FP8) shm = D == 64 ? mfma_lds_bytes<DT_FP8, 64>(G, S, true) : mfma_lds_bytes<DT_FP8, 128>(G, S, true);
-  else shm = D == 64 ? mfma_lds_bytes<DT_BF16, 64>(G, S, true) : mfma_lds_bytes<DT_BF16, 128>(G, S, true);
   int best = 0;
   for (int i = 0; i < 2; ++i) {
     int n = 0;
