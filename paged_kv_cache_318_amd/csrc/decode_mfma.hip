@@ -51,10 +51,11 @@ constexpr int mfma_blocks_per_iter(int elem_bytes) { return elem_bytes == 2 ? 2 
 
 // fp8 caches with 16-token blocks stage the value tiles through LDS too (next to the keys), so
 // that every K/V load of the segment loop is a direct-to-LDS load and the loop can issue each
-// iteration's loads one step ahead (fp8 batch: 134.7-135.1 -> 129.7-130.1 us). With register loads
-// in flight beside direct-to-LDS loads the compiler drains every load before the first read of a
-// staged tile, which is why the values go through LDS too. At 16 bits the second stage would
-// leave two work-groups per CU.
+// iteration's loads one step ahead (fp8 batch: 134.7-135.1 -> 129.7-130.1 us), the keys into a
+// ring of two slots (a further 1 us). With register loads in flight beside direct-to-LDS loads
+// the compiler drains every load before the first read of a staged tile, which is why the values
+// go through LDS too. Per wave: two key slots and one value stage of two tiles, 12 KB (three
+// work-groups per CU still fit); at 16 bits the same stages would leave two work-groups per CU.
 constexpr bool mfma_stages_values(int cdt, int block_size) { return cdt == DT_FP8 && block_size == 16; }
 
 // Bytes of dynamic LDS: the staged key (and staged value) tiles of one iteration per wave (reused
@@ -63,7 +64,7 @@ constexpr bool mfma_stages_values(int cdt, int block_size) { return cdt == DT_FP
 template <int CDT, int D, int B>
 constexpr size_t mfma_lds_bytes(int G, int S, bool sched_lds) {
   const size_t stage = size_t{4} * mfma_blocks_per_iter(Elem<CDT>::bytes) * 16 * D * Elem<CDT>::bytes *
-                       (mfma_stages_values(CDT, B) ? 2 : 1);
+                       (mfma_stages_values(CDT, B) ? 3 : 1);
   const size_t merge = (128 + size_t{4} * G * D) * sizeof(float);
   const size_t sched = sched_lds ? static_cast<size_t>(ordered_lds_ints(S)) * sizeof(int) : 0;
   return (stage > merge ? stage : merge) + sched;
@@ -143,8 +144,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // (l % CPR) ^ (row % CPR) of its row, so LDS holds each row XOR-swizzled by its index and the
   // score-operand reads below (16 rows at one chunk column) fall into distinct banks. PAIR: rows
   // 0-7 come from the first block, 8-15 from the second (dsec: this lane's row is in the second).
-  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT * (kStageValues ? 2 : 1));
-  [[maybe_unused]] uint8_t* vbuf = kbuf + NBI * KT;  // the staged value tiles (kStageValues)
+  uint8_t* kbuf = reinterpret_cast<uint8_t*>(smem) + wave * (NBI * KT * (kStageValues ? 3 : 1));
+  [[maybe_unused]] uint8_t* vbuf = kbuf + 2 * NBI * KT;  // the staged value tiles (kStageValues)
   int dsrc[NI];
   bool dsec[NI];
 #pragma unroll
@@ -173,12 +174,12 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
   // ---- the math of one iteration, shared by both loops below ----
   // scores of the iteration's tiles from the staged keys
-  auto tile_scores = [&](int nlive, f32x4 (&zt)[NBI]) {
+  auto tile_scores = [&](const uint8_t* kst, int nlive, f32x4 (&zt)[NBI]) {
 #pragma unroll
     for (int u = 0; u < NBI; ++u) {
       zt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (u / SUB >= nlive) continue;
-      const uint8_t* kb = kbuf + u * KT;
+      const uint8_t* kb = kst + u * KT;
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + kread[i]);
@@ -283,8 +284,8 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
   if constexpr (kStageValues) {
   // ---- fp8 keys and values both staged through LDS, each iteration's loads issued one step
-  // ahead: the next iteration's keys once this one's scores have read the key slots, its values
-  // once this one's value operands are in registers. Every K/V load of the loop is then a
+  // ahead: the next iteration's keys as soon as this one's keys have landed (they go to the other
+  // key slot), its values once this one's value operands are in registers. Every K/V load of the loop is then a
   // direct-to-LDS load whose completion the explicit counts below track; the table entries and
   // the query operands (register loads) are waited for before the first of them. ----
   typedef __attribute__((address_space(4))) const float cfloat_t;  // (scalar loads of the scales)
@@ -305,12 +306,13 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
       tb[u] = (static_cast<size_t>(pb[u]) * Hkv + g) * KTB;
     }
   };
-  auto issue_keys = [&](int nl, const size_t (&tb)[NBI]) {
+  auto kslot = [&](int itx) { return kbuf + ((itx / BPI) & 1) * (NBI * KT); };
+  auto issue_keys = [&](uint8_t* kdst, int nl, const size_t (&tb)[NBI]) {
 #pragma unroll
     for (int u = 0; u < NBI; ++u)
       if (u < nl) {
 #pragma unroll
-        for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + tb[u] + dsrc[ii], kbuf + u * KT + 1024 * ii);
+        for (int ii = 0; ii < NI; ++ii) dma16<kKeyAux>(a.k_cache + tb[u] + dsrc[ii], kdst + u * KT + 1024 * ii);
       }
   };
   auto issue_values = [&](int nl, const size_t (&tb)[NBI]) {  // [D][16] codes as stored, 1 KB a load
@@ -336,7 +338,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     const int nl = min(BPI, cnt);
     int pba[NBI];
     tiles_at(0, nl, pba, ba);
-    issue_keys(nl, ba);
+    issue_keys(kslot(0), nl, ba);
     issue_values(nl, ba);
     scales_of(pba, zs_l, vs_l);
   }
@@ -351,6 +353,16 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
     // this iteration's keys have landed (its values, issued after them, may still be in flight)
     if (u_new < 0 && nlive == BPI) __builtin_amdgcn_s_waitcnt(kWaitKeys);
     else __builtin_amdgcn_s_waitcnt(0);
+    // the next iteration's keys, into the other key slot
+    int pba_n[NBI];
+    size_t ba_n[NBI];
+    float zs_n[NBI], vs_n[NBI];
+    if (nl_next > 0) {
+      tiles_at(it + BPI, nl_next, pba_n, ba_n);
+      issue_keys(kslot(it + BPI), nl_next, ba_n);
+      scales_of(pba_n, zs_n, vs_n);
+    }
+    uint8_t* kcur = kslot(it);
     if (u_new >= 0) {  // the new token's key row into the staged tile and into the cache
       const size_t pbn = static_cast<size_t>(slot_new / B);
       const float ks = a.k_scale[pbn * Hkv + g];
@@ -360,23 +372,13 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
         Raw<16> in;
         in.w[0] = kn.x; in.w[1] = kn.y; in.w[2] = kn.z; in.w[3] = kn.w;
         const Raw<8> kc = new_key_piece<CDT, QDT, 8>(in, ks);
-        store_raw<8>(kbuf + u_new * KT + o_new * CPR * 16 + 16 * ((lane / 2) ^ (o_new % CPR)) + 8 * (lane % 2), kc);
+        store_raw<8>(kcur + u_new * KT + o_new * CPR * 16 + 16 * ((lane / 2) ^ (o_new % CPR)) + 8 * (lane % 2), kc);
         store_raw<8>(const_cast<uint8_t*>(a.k_cache) + (pbn * Hkv + g) * KTB + (slot_new % B) * D + 8 * lane, kc);
       }
       __builtin_amdgcn_s_waitcnt(0);
     }
     f32x4 zt[NBI];
-    tile_scores(nlive, zt);
-    // the key slots are read: the next iteration's keys
-    int pba_n[NBI];
-    size_t ba_n[NBI];
-    float zs_n[NBI], vs_n[NBI];
-    if (nl_next > 0) {
-      __builtin_amdgcn_s_waitcnt(kWaitLds);
-      tiles_at(it + BPI, nl_next, pba_n, ba_n);
-      issue_keys(nl_next, ba_n);
-      scales_of(pba_n, zs_n, vs_n);
-    }
+    tile_scores(kcur, nlive, zt);
     int valid[NBI];
     float pz[4 * NBI];
     online_softmax(ia, nlive, zt, zs_l, valid, pz);
@@ -545,7 +547,7 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
     // scores of the iteration's tiles
     f32x4 zt[NBI];
-    tile_scores(nlive, zt);
+    tile_scores(kbuf, nlive, zt);
     int valid[NBI];
     float pz[4 * NBI];
     online_softmax(ia, nlive, zt, zs_l, valid, pz);
