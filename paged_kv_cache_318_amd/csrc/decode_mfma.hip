@@ -10,7 +10,8 @@
 // One work-group (4 wave64s) handles one (kv head, sequence, partition); wave w takes work items
 // (blocks; pairs of blocks at B = 8) w, w+4, ... of the partition, two 16-token tiles per
 // iteration, so each K/V tile is fetched from HBM once for all G heads and every wave keeps two
-// tiles (16 KB at 16 bits) in flight.
+// tiles (16 KB at 16 bits) in flight (fp8 with 16-token blocks: the next iteration's tiles fly
+// while this one computes; see mfma_stages_values).
 //
 // Operand layouts (v_mfma_f32_16x16x32_{bf16,f16}: lane l = 16*q4 + n holds 8 elements of row
 // n of A and of column n of B, the k-range given by q4; the 16x16 result gives lane (q4, n) rows
@@ -284,10 +285,11 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
 
   if constexpr (kStageValues) {
   // ---- fp8 keys and values both staged through LDS, each iteration's loads issued one step
-  // ahead: the next iteration's keys as soon as this one's keys have landed (they go to the other
-  // key slot), its values once this one's value operands are in registers. Every K/V load of the loop is then a
-  // direct-to-LDS load whose completion the explicit counts below track; the table entries and
-  // the query operands (register loads) are waited for before the first of them. ----
+  // ahead: the next iteration's keys as soon as this one's keys have landed (they go to the
+  // other key slot), its values once this one's value operands are in registers. Every K/V load
+  // of the loop is then a direct-to-LDS load whose completion the explicit counts below track;
+  // the table entries and the query operands (register loads) are waited for before the first of
+  // them. ----
   typedef __attribute__((address_space(4))) const float cfloat_t;  // (scalar loads of the scales)
   constexpr int NVI = KT / 1024;  // value load instructions per tile
   // vmcnt(N) lgkmcnt(0): every direct load but the last N issued, and every LDS access
