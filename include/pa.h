@@ -326,9 +326,10 @@ int pa_swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    void* stream);
 
 /*
- * Profiling: when enabled, every pa_* launch is bracketed by HIP events on its stream.
- * pa_profile_read synchronises on those events and returns, for one kernel kind, the summed
- * device time in milliseconds and the number of launches since the last reset.
+ * Profiling: when enabled, every pa_* call's kernel launch carries a pair of HIP events that the
+ * runtime stamps at that kernel's own start and end (hipExtLaunchKernel). pa_profile_read
+ * synchronises on those events and returns, for one kernel kind, the summed kernel time in
+ * milliseconds and the number of launches since the last reset.
  */
 typedef enum {
   PA_KERNEL_DECODE_PARTITION = 0, /* the attention kernel (VALU or MFMA variant)      */

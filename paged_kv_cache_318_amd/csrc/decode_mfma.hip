@@ -730,21 +730,21 @@ static hipError_t launch_mfma_dnb(const DecodeArgs& a, hipStream_t st) {
     // alone has at most a.max_parts - 1 parts, so the grid's part dimension stops there
     const dim3 grid(a.num_kv_heads, a.num_groups + a.num_seqs, a.max_parts - 1 > 0 ? a.max_parts - 1 : 1);
     const size_t shm = mfma_lds_bytes<CDT, D, B>(16, 0, false);  // up to 16 rows
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_grouped_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) launch_kernel((decode_mfma_grouped_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+    else launch_kernel((decode_mfma_grouped_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
     return hipGetLastError();
   }
   const size_t shm = mfma_lds_bytes<CDT, D, B>(G, a.num_seqs, a.balanced != 0);
   if (a.balanced) {
     const dim3 grid(a.nw);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
-    else hipLaunchKernelGGL((decode_mfma_balanced_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
+    if (a.stream_kv) launch_kernel((decode_mfma_balanced_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+    else launch_kernel((decode_mfma_balanced_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
   } else {
     const dim3 grid = a.ordered ? dim3(a.num_kv_heads * a.num_seqs * a.max_parts)
                                 : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
     const size_t shm_f = mfma_lds_bytes<CDT, D, B>(G, a.num_seqs, a.ordered != 0);
-    if (a.stream_kv) hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm_f, st, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm_f, st, a);
+    if (a.stream_kv) launch_kernel((decode_mfma_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm_f, st, a);
+    else launch_kernel((decode_mfma_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm_f, st, a);
   }
   return hipGetLastError();
 }

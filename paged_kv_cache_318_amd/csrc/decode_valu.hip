@@ -375,8 +375,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int block
 template <int CDT, int QDT, int D, int B>
 static void launch_valu_nt(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   const size_t shm = a.ordered ? static_cast<size_t>(ordered_lds_ints(a.num_seqs)) * sizeof(int) : 0;
-  if (a.stream_kv) hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
-  else hipLaunchKernelGGL((decode_valu_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
+  if (a.stream_kv) launch_kernel((decode_valu_kernel<CDT, QDT, D, B, true>), grid, dim3(256), shm, st, a);
+  else launch_kernel((decode_valu_kernel<CDT, QDT, D, B, false>), grid, dim3(256), shm, st, a);
 }
 
 template <int CDT, int QDT, int D>
@@ -411,8 +411,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int cdt, int qdt, int D, int 
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int D, int B, hipStream_t st) {
   const dim3 grid(a.num_heads, a.num_seqs);
-  if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, st, a, B);
-  else if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(128), 0, st, a, B);
+  if (D == 64) launch_kernel((decode_merge_kernel<64>), grid, dim3(64), 0, st, a, B);
+  else if (D == 128) launch_kernel((decode_merge_kernel<128>), grid, dim3(128), 0, st, a, B);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -160,7 +160,7 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
                            hipStream_t st) {
   const dim3 grid((T + B - 1) / B, Hkv), block(256);
 #define PA_WRITE(I, C)                                                                         \
-  hipLaunchKernelGGL((write_kv_kernel<I, C>), grid, block, 0, st, k_new, v_new, k_cache,       \
+  launch_kernel((write_kv_kernel<I, C>), grid, block, 0, st, k_new, v_new, k_cache,       \
                      v_cache, slots, T, Hkv, D, B, NB, k_scale, v_scale)
   if (cache_dt == DT_FP8) {
     if (in_dt == DT_F32) PA_WRITE(DT_F32, DT_FP8);
@@ -198,7 +198,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
   const bool fp8 = cache_dt == DT_FP8;
   uint8_t* k = reinterpret_cast<uint8_t*>(k_cache);
   uint8_t* v = reinterpret_cast<uint8_t*>(v_cache);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
+  launch_kernel(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
                      st, k, v, k, v, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
                      fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, pairs, NB, NB, Hkv,
                      block_bytes);
@@ -211,7 +211,7 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k,
                               int dst_nb, int Hkv, int D, int B, int cache_dt, hipStream_t st) {
   const size_t block_bytes = block_bytes_of(Hkv, D, B, cache_dt);
   const bool fp8 = cache_dt == DT_FP8;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
+  launch_kernel(copy_blocks_kernel, dim3(num_pairs, copy_chunks(block_bytes)), dim3(256), 0,
                      st, reinterpret_cast<const uint8_t*>(src_k),
                      reinterpret_cast<const uint8_t*>(src_v), reinterpret_cast<uint8_t*>(dst_k),
                      reinterpret_cast<uint8_t*>(dst_v), fp8 ? src_ks : nullptr,
@@ -226,7 +226,7 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* k_cache, const
   const int mbt = (max_tokens + B - 1) / B;
   const dim3 grid(mbt < MB ? mbt : MB, S), block(256);
 #define PA_GATHER(T)                                                                            \
-  hipLaunchKernelGGL((gather_kv_kernel<T>), grid, block, 0, st, reinterpret_cast<T*>(k_out),    \
+  launch_kernel((gather_kv_kernel<T>), grid, block, 0, st, reinterpret_cast<T*>(k_out),    \
                      reinterpret_cast<T*>(v_out), reinterpret_cast<const T*>(k_cache),          \
                      reinterpret_cast<const T*>(v_cache), tables, lens, Hkv, D, B, MB, NB,     \
                      max_tokens)

@@ -75,7 +75,9 @@ Profiler& prof() {
   return p;
 }
 
-bool begin_event(hipStream_t st, EventPair* ev) {
+// Every timed pa_* call launches exactly one kernel: its event pair goes to that launch, which
+// has the runtime stamp the kernel's own start and end (not the enqueue of a marker beside it).
+bool begin_event(hipStream_t, EventPair* ev) {
   Profiler& P = prof();
   if (!P.on) return false;
   if (!P.pool.empty()) {
@@ -83,14 +85,24 @@ bool begin_event(hipStream_t st, EventPair* ev) {
     P.pool.pop_back();
   } else {
     if (hipEventCreate(&ev->start) != hipSuccess) return false;
-    if (hipEventCreate(&ev->stop) != hipSuccess) return false;
+    if (hipEventCreate(&ev->stop) != hipSuccess) {
+      (void)hipEventDestroy(ev->start);
+      return false;
+    }
   }
-  return hipEventRecord(ev->start, st) == hipSuccess;
+  pa::dispatch_events() = pa::DispatchEvents{ev->start, ev->stop};
+  return true;
 }
 
-void end_event(bool active, hipStream_t st, const EventPair& ev, int kind) {
+void end_event(bool active, hipStream_t, const EventPair& ev, int kind) {
   if (!active) return;
-  if (hipEventRecord(ev.stop, st) == hipSuccess) prof().pending[kind].push_back(ev);
+  pa::DispatchEvents& pending = pa::dispatch_events();
+  if (pending.start == nullptr) {
+    prof().pending[kind].push_back(ev);  // the launch took the pair
+  } else {
+    pending = pa::DispatchEvents{};  // nothing was launched: the pair goes back unused
+    prof().pool.push_back(ev);
+  }
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -710,6 +722,11 @@ int pa_profile_read(int kernel_kind, double* total_ms, long long* launches) {
 // Not an entry point of the ABI: the allocation-free decode (decode_noalloc.hip) reaches pa_decode's
 // host logic through here.
 namespace pa {
+
+DispatchEvents& dispatch_events() {
+  thread_local DispatchEvents pending;
+  return pending;
+}
 
 int decode_with_library_workspace(void* out, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,

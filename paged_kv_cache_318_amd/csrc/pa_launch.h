@@ -2,12 +2,31 @@
 // given stream and returns hipGetLastError(); all arguments were validated by pa_api.cpp.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pa_device.h"
 
 namespace pa {
+
+// Events the next kernel launch of this thread hands to the runtime, which stamps them at that
+// kernel's own start and end (hipExtLaunchKernel); both null: a plain launch. The profiler in
+// pa_api.cpp sets them around a pa_* call's one kernel; the launch clears them.
+struct DispatchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+DispatchEvents& dispatch_events();
+
+// Every kernel of the library is launched through this.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t st,
+                          Args... args) {
+  DispatchEvents& pending = dispatch_events();
+  const DispatchEvents ev = pending;
+  pending = DispatchEvents{};
+  hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev.start, ev.stop, 0u, args...);
+}
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,
                               int block_size, hipStream_t st);

@@ -504,7 +504,7 @@ static hipError_t launch_prefill_dnb(const PrefillArgs& a, int max_query_len, hi
   if (tiles > INT_MAX || wgs > INT_MAX) return hipErrorInvalidValue;
   args.num_tiles = static_cast<int>(tiles);
   const size_t shm = prefill_lds_bytes<CDT, D>();
-  hipLaunchKernelGGL((prefill_mfma_kernel<CDT, QDT, D, B>), dim3(static_cast<unsigned>(wgs)),
+  launch_kernel((prefill_mfma_kernel<CDT, QDT, D, B>), dim3(static_cast<unsigned>(wgs)),
                      dim3(256), shm, st, args);
   return hipGetLastError();
 }
