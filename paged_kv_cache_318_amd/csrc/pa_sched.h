@@ -178,6 +178,22 @@ __device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int
   const int per = (S + nt - 1) / nt;
   const int beg = min(S, tid * per), end = min(S, beg + per);
   const int cap = a.max_blocks * B;
+  {
+    // The list's length, by every wave on its own (no LDS, no barrier): a work-group past the
+    // end leaves here. The grid is sized by the table width, so on long-tailed length mixes most
+    // of it lies past the end; the full ordering below would cost each of them 2 us.
+    const int lane = tid & 63;
+    int items = 0;
+    for (int s = lane; s < S; s += 64) {
+      int L = a.lens[s];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      const int nblk = (L + B - 1) / B;
+      items += nblk == 0 ? 1 : nblk / pb + (nblk % pb != 0 ? 1 : 0);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) items += __shfl_xor(items, off);
+    if (k >= items) return make_int2(-1, 0);
+  }
   if (tid <= kOrderBuckets) bcnt[tid] = 0;
   __syncthreads();
   // bucket of a sequence's last item: blocks in its partial partition, longest first; a sequence
