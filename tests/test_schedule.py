@@ -151,6 +151,31 @@ def test_ordered_list_holds_every_item_once(pb):
         assert cls == sorted(cls)
 
 
+def early_exit_count(lens, B, pb, cap):
+    """The item count each wave computes before the ordering (the early exit past the list's end)."""
+    items = 0
+    for L in lens:
+        L = 0 if L < 0 else min(L, cap)
+        n = (L + B - 1) // B
+        items += 1 if n == 0 else n // pb + (1 if n % pb else 0)
+    return items
+
+
+@pytest.mark.parametrize("pb", [1, 2, 3, 16, 64, 128])
+def test_early_exit_count_is_the_list_length(pb):
+    """A work-group leaves before the ordering only when its item index is at least this count, so
+    the count must equal the ordered list's length exactly (a smaller one would drop real items),
+    lengths clamped to the table width as the kernels clamp them (negative ones to 0)."""
+    rng = random.Random(1000 + pb)
+    B = 16
+    for _ in range(30):
+        S = rng.randint(1, 300)
+        cap = B * rng.randint(1, 60 * pb)
+        lens = [rng.choice([0, -5, rng.randint(1, 2 * cap)]) for _ in range(S)]
+        clamped = [0 if L < 0 else min(L, cap) for L in lens]
+        assert early_exit_count(lens, B, pb, cap) == len(ordered_items(clamped, B, pb))
+
+
 def xcd_items_per_period():
     return 8 * XCD_ROUNDS - 4
 
