@@ -178,6 +178,7 @@ __device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int
   const int per = (S + nt - 1) / nt;
   const int beg = min(S, tid * per), end = min(S, beg + per);
   const int cap = a.max_blocks * B;
+  int own_len = 0;  // with one sequence a thread (per == 1): the clamped length of sequence tid
   {
     // The list's length, by every wave on its own (no LDS, no barrier): a work-group past the
     // end leaves here. The grid is sized by the table width, so on long-tailed length mixes most
@@ -187,6 +188,7 @@ __device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int
     for (int s = lane; s < S; s += 64) {
       int L = a.lens[s];
       L = L < 0 ? 0 : (L > cap ? cap : L);
+      if (s == tid) own_len = L;
       const int nblk = (L + B - 1) / B;
       items += nblk == 0 ? 1 : nblk / pb + (nblk % pb != 0 ? 1 : 0);
     }
@@ -204,8 +206,11 @@ __device__ inline int2 ordered_item(const DecodeArgs& a, int B, long long k, int
   };
   int nfull = 0;
   for (int s = beg; s < end; ++s) {
-    int L = a.lens[s];
-    L = L < 0 ? 0 : (L > cap ? cap : L);
+    int L = own_len;  // (loaded above when per == 1, where s == tid)
+    if (per > 1) {
+      L = a.lens[s];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+    }
     lens_l[s] = L;
     const int nblk = (L + B - 1) / B;
     nfull += nblk / pb;
