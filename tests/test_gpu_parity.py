@@ -829,6 +829,36 @@ def test_profile_counts_launches(fused):
     assert ms > 0 and ms_m > 0 and (fused or ms_w > 0)
 
 
+def test_profile_times_lie_within_the_steps():
+    """The profiler's events are stamped at each kernel's own start and end: over several steps the
+    summed kernel times are positive and no longer than the steps' wall time on the stream."""
+    w = cfg(2, num_seqs=8)
+    d = upload(w)
+    ws = workspace_for(d.q, d.k_cache, d.tables, w.block_size, 512)
+    out = torch.empty(w.num_seqs, w.num_heads, w.head_dim, dtype=torch.float16, device="cuda")
+
+    def step():
+        decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
+                    d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=512, workspace=ws,
+                    fused=False)
+
+    step()
+    torch.cuda.synchronize()
+    lib.pa_profile_enable(True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(4):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    kinds = (lib.PA_KERNEL_DECODE_PARTITION, lib.PA_KERNEL_DECODE_MERGE, lib.PA_KERNEL_WRITE_KV)
+    reads = [lib.pa_profile_read(k) for k in kinds]
+    lib.pa_profile_enable(False)
+    assert [n for _, n in reads] == [4, 4, 4]
+    assert all(ms > 0 for ms, _ in reads)
+    assert sum(ms for ms, _ in reads) <= t0.elapsed_time(t1)
+
+
 # ----------------------------------------------------------------------------------------------
 # many steps through the block manager: forks, copy-on-write, frees with block reuse, a swap out
 # and back -- the device pools and outputs follow the oracle's host pools step by step
