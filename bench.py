@@ -39,7 +39,8 @@ def parse_args():
     # still ran 9% slower than the steady state that the per-step percentiles show
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the headline batch)")
-    p.add_argument("--dtype", default=None, help="override the cache dtype of config 2 (f16|bf16)")
+    p.add_argument("--dtype", default=None,
+                   help="override the cache dtype of config 2, or of --measure prefill (f16|bf16)")
     p.add_argument("--first-step", action="store_true", help="config 4: every sample at its first step")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
@@ -165,20 +166,25 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak, publishe
 
 def measure_prefill(args, lib, torch):
     """Chunked prefill: 16 sequences append 512-token chunks to contexts of 0..3584 tokens (32
-    query / 8 kv heads x 128, bf16, block size 16). A step writes the chunks' K/V (pa_write_kv)
-    and runs causal attention of every new token over its sequence (pa_prefill)."""
+    query / 8 kv heads x 128, bf16 unless --dtype f16, block size 16). A step writes the chunks'
+    K/V (pa_write_kv) and runs causal attention of every new token over its sequence
+    (pa_prefill)."""
     import numpy as np
 
     from workloads import make_prefill
     from workloads.device import upload
     rng = np.random.default_rng(15)
     ctx = rng.integers(0, 3584, endpoint=True, size=16)
-    w = make_prefill(ctx, [512] * 16, num_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+    dt = args.dtype or "bf16"
+    if dt not in ("bf16", "f16"):
+        raise SystemExit("--measure prefill takes --dtype bf16 or f16")
+    w = make_prefill(ctx, [512] * 16, num_heads=32, num_kv_heads=8, head_dim=128, dtype=dt,
                      block_size=args.block_size or 16, seed=15)
     reps = [upload(w) for _ in range(max(1, args.replicas))]
     qs = torch.from_numpy(np.ascontiguousarray(w.query_start, dtype=np.int32)).cuda()
     T = w.q.shape[0]
-    out = torch.empty(T, w.num_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(T, w.num_heads, w.head_dim,
+                      dtype=torch.bfloat16 if dt == "bf16" else torch.float16, device="cuda")
 
     def step(i):
         d = reps[i % len(reps)]
@@ -210,9 +216,9 @@ def measure_prefill(args, lib, torch):
         "metric": "chunked prefill attention: TFLOP/s (causal pairs x 4 x head_dim x heads), new tokens/s",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/q, scattered blocks; no dataset)",
+        "dtype": dt, "data": "synthetic (seeded N(0,1) K/V/q, scattered blocks; no dataset)",
         "new_tokens_per_s": round(T / (ms_step * 1e-3), 1),
-        "config": {"workload": "prefill-16x512-gqa-bf16", "num_seqs": 16, "chunk": 512,
+        "config": {"workload": f"prefill-16x512-gqa-{dt}", "num_seqs": 16, "chunk": 512,
                    "context": "U[0,3584]", "num_heads": 32, "num_kv_heads": 8, "head_dim": 128,
                    "block_size": w.block_size, "new_tokens": T, "causal_pairs": w.attended_pairs(),
                    "flops": flops, "bytes": w.prefill_bytes()},
@@ -220,7 +226,7 @@ def measure_prefill(args, lib, torch):
                        "write_kv": round(1e3 * w_ms / max(w_n, 1), 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_mfma", "prefill-16x512-gqa-bf16",
+                     "traffic": measured_traffic("prefill_mfma", f"prefill-16x512-gqa-{dt}",
                                                  "prefill_hbm_traffic.txt"),
                      "kernel": "prefill_mfma",
                      "bytes_gbs": round(w.prefill_bytes() / (k_ms * 1e-3) / 1e9, 1)},

@@ -88,7 +88,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int ROWS = prefill_rows<CDT, D>();
   constexpr int EB = Elem<CDT>::bytes;
   constexpr int KK = D / 32;                 // score MFMAs per 16-token tile
-  constexpr int MI = D / 16;                 // value MFMA tiles (x2 for hi / remainder)
+  constexpr int MI = D / 16;                 // value MFMA tiles (x2 for bf16 hi / remainder)
+  // The weights P reach the value MFMA as 16-bit operands: fp16 weights keep 11 significant bits,
+  // enough for the 2e-3 tolerance, and go as one operand; bf16 weights (8 bits) go as a rounded
+  // part plus its remainder, two MFMAs.
+  constexpr bool kSplitP = QDT == DT_BF16;
   constexpr int KL = EB == 2 ? KK : KK / 2;  // 16-byte key chunks per lane per tile
   constexpr int KT = 16 * D * EB;            // bytes of one 16-token key (or value) tile in LDS
   constexpr int KTB = B * D * EB;            // bytes of one (block, kv head) tile in the cache
@@ -404,16 +408,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         pz[i] = ok[i] ? e : 0.0f;
         lsum[c] += pz[i];
       }
-      // P^T as 16-bit hi part + remainder
+      // P^T: one fp16 operand, or bf16 hi part + remainder
       uint32_t phw[4], plw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float vsc = i < 2 ? vs[0] : vs[1];
         const float p0 = pz[2 * i] * vsc, p1 = pz[2 * i + 1] * vsc;
-        split16x2<QDT>(p0, p1, phw[i], plw[i]);
+        if constexpr (kSplitP) split16x2<QDT>(p0, p1, phw[i], plw[i]);
+        else phw[i] = pack16x2<QDT>(p0, p1);
       }
       phi[c] = u32x4{phw[0], phw[1], phw[2], phw[3]};
-      plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
+      if constexpr (kSplitP) plo[c] = u32x4{plw[0], plw[1], plw[2], plw[3]};
     }
     // weighted values over the 32 tokens of the two tiles; slots at or beyond L (never
     // written) get zero values
@@ -451,8 +456,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       else return u32x4{a0, a1, c0, c1};
     };
     // each value operand read once from LDS and multiplied into every column set; groups of
-    // 4 value tiles (hi MFMAs of the group, then its remainder MFMAs) so no MFMA waits on the
-    // one just issued into the same accumulator
+    // 4 value tiles (for bf16, hi MFMAs of the group, then its remainder MFMAs) so no MFMA waits
+    // on the one just issued into the same accumulator
     constexpr int GV = CW == 1 ? 4 : 2;
 #pragma unroll
     for (int m0 = 0; m0 < MI; m0 += GV) {
@@ -463,10 +468,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], phi[c], acc[c][m0 + j]);
       }
+      if constexpr (kSplitP) {
 #pragma unroll
-      for (int j = 0; j < GV; ++j)
+        for (int j = 0; j < GV; ++j)
 #pragma unroll
-        for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], plo[c], acc[c][m0 + j]);
+          for (int c = 0; c < CW; ++c) acc[c][m0 + j] = mfma_k32<QDT>(vop[j], plo[c], acc[c][m0 + j]);
+      }
     }
   };
   // Interior iterations (every token of both tiles at or before the wave's earliest query, so

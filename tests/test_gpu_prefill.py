@@ -12,6 +12,8 @@ cache), negative, zero and large scales, NaN-poisoned unused memory, placement i
 full-size chunked-prefill batch checked on sampled rows.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -234,6 +236,42 @@ def test_poison_and_placement_invariance_bit_exact(dtype):
             w.slots = (inv[w.slots // w.block_size] * w.block_size + w.slots % w.block_size).astype(np.int32)
         outs.append(run_gpu(w, out_dt="f32"))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_bf16_values_beyond_fp16_range():
+    """bf16 has fp32's exponent range: two context tokens hold +-70144 (past fp16's largest value)
+    in two dims here. The rows that attend them are finite and match the oracle within 2e-3 plus
+    2^-14 of sum_t p_t |v_t| (the oracle run on |V|), and every other row has the very bits it has
+    without the large values (a column's arithmetic depends on its own data alone)."""
+    ctx, new = [300, 40, 1000], [64, 19, 100]
+    kw = dict(num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=31)
+    base = make_prefill(ctx, new, **kw)
+    w = make_prefill(ctx, new, **kw)
+    B, G = w.block_size, w.num_heads // w.num_kv_heads
+    big = [(0, 1, 150), (2, 0, 900)]  # (sequence, kv head, context position)
+    for s, h, p in big:
+        blk = int(w.tables[s, p // B])
+        w.v_pool[blk, h, 3, p % B] = 0x4789   # +70144
+        w.v_pool[blk, h, 77, p % B] = 0xC789  # -70144
+    out0 = run_gpu(base, out_dt="f32")
+    out = run_gpu(w, out_dt="f32")
+    ref = run_oracle(w)
+    mag = run_oracle(dataclasses.replace(w, v_pool=w.v_pool & np.uint16(0x7FFF),
+                                         v_new=w.v_new & np.uint16(0x7FFF)))
+    qs = w.query_start
+    hit = np.zeros(out.shape[:2], dtype=bool)  # [token row, query head] attends a large value
+    for s, h, p in big:
+        L, n = int(w.lens[s]), int(qs[s + 1] - qs[s])
+        for t in range(int(qs[s]), int(qs[s + 1])):
+            if L - n + (t - int(qs[s])) >= p:
+                hit[t, h * G:(h + 1) * G] = True
+    assert hit.any() and (~hit).any()
+    assert np.all(np.isfinite(out[hit]))
+    err = np.abs(out[hit] - ref[hit])
+    lim = 2e-3 + 2.0 ** -14 * mag[hit]
+    assert np.all(err <= lim), f"max err {err.max():.3e}, worst ratio {np.max(err / lim):.3f}"
+    assert_close(out[~hit], ref[~hit], "bf16", "f32", "rows without large values")
+    assert np.array_equal(out[~hit], out0[~hit])
 
 
 def test_full_size_chunked_prefill_sampled_rows():
