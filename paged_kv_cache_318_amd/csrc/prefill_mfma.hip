@@ -389,9 +389,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       // The accumulators are rescaled to a new running max only when some column of the set
       // sees a score above its max by more than kSlack (log2 units); until then its weights run
       // up to 2^kSlack (the result is the same for any common shift, the final division takes
-      // it out). bf16 has fp32's range; fp16 weights keep the eager rescale, so that a weight
-      // times a large fp8 value scale cannot overflow.
-      constexpr float kSlack = QDT == DT_BF16 ? 8.0f : 0.0f;
+      // it out). bf16 has fp32's range and fp16 holds 2^8; only fp16 weights times an fp8 value
+      // scale keep the eager rescale, so that their product cannot overflow.
+      constexpr float kSlack = (QDT == DT_BF16 || CDT != DT_FP8) ? 8.0f : 0.0f;
       if (__builtin_amdgcn_ballot_w64(tm > m[c] + kSlack) != 0) {
         const float mn = fmaxf(m[c], tm);  // finite: block 0 holds token 0, which every column attends
         const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
