@@ -78,10 +78,11 @@ __device__ int seq_by_length_rank(const int32_t* lens, int S, int r, int lane, i
   return r;  // not reached: the ranks are a permutation of 0 .. S-1
 }
 
-// Two column sets: 2 wave64s per SIMD (at most 256 registers a lane). One set (fp8, D = 128):
-// also 2, for the registers of its converted operands.
+// Three wave64s per SIMD (at most 168 registers a lane): the two-column-set instances at D = 128
+// need a few more, and the compiler spills 5 of them around the second loop, never inside
+// either loop (two waves per SIMD with no spill ran 5% slower).
 template <int CDT, int QDT, int D, int B>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(B == 8 || B == 16 || B == 32, "block size");
   constexpr int NBL = 32 / B;                // blocks an iteration (32 tokens) touches
   constexpr int CW = prefill_column_sets<CDT, D>();
@@ -376,38 +377,62 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           z[4 * u + i] = EB == 2 ? zt[c][u][i] : zt[c][u][i] * zs[u];
         }
       }
-      float zm[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zm[i] = ok[i] ? z[i] : neg_inf();
-      // a chain, which the compiler folds into 3-input maxes
-      float tm = zm[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tm = fmaxf(tm, zm[i]);
-      tm = pair32_max(pair16_max(tm));
-      // -inf * 0 (every token of a column masked, zero scale) is NaN: compares false below
-      if constexpr (EB == 2) tm *= zsp;
       // The accumulators are rescaled to a new running max only when some column of the set
       // sees a score above its max by more than kSlack (log2 units); until then its weights run
       // up to 2^kSlack (the result is the same for any common shift, the final division takes
       // it out). bf16 has fp32's range and fp16 holds 2^8; only fp16 weights times an fp8 value
       // scale keep the eager rescale, so that their product cannot overflow.
       constexpr float kSlack = (QDT == DT_BF16 || CDT != DT_FP8) ? 8.0f : 0.0f;
-      if (__builtin_amdgcn_ballot_w64(tm > m[c] + kSlack) != 0) {
+      // weights of the lane's 8 tokens from the running max as it stands, and their sum
+      float pz[8];
+      auto weights = [&]() {
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = EB == 2 ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], zsp, -m[c]))
+                                  : __builtin_amdgcn_exp2f(z[i] - m[c]);
+          pz[i] = ok[i] ? e : 0.0f;
+          ps += pz[i];
+        }
+        return ps;
+      };
+      // the columns' max over the iteration's tokens, and the rescale if some column needs it
+      // (returns whether it rescaled)
+      auto rescale = [&]() {
+        float zm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zm[i] = ok[i] ? z[i] : neg_inf();
+        // a chain, which the compiler folds into 3-input maxes
+        float tm = zm[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) tm = fmaxf(tm, zm[i]);
+        tm = pair32_max(pair16_max(tm));
+        // -inf * 0 (every token of a column masked, zero scale) is NaN: compares false below
+        if constexpr (EB == 2) tm *= zsp;
+        if (__builtin_amdgcn_ballot_w64(tm > m[c] + kSlack) == 0) return false;
         const float mn = fmaxf(m[c], tm);  // finite: block 0 holds token 0, which every column attends
         const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
         lsum[c] *= alpha;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) acc[c][mi] = acc[c][mi] * alpha;
         m[c] = mn;
+        return true;
+      };
+      float ps;
+      if constexpr (kSlack > 0.0f) {
+        // Weights first: while every lane's 8 weights sum to at most 2^kSlack (so each is at
+        // most that), the max is not needed at all. Otherwise (a large score, the first
+        // iteration's -inf max, or inf / NaN) the max decides, and the weights are taken again
+        // if it moved. That rare path takes the set's scores again from LDS (the same MFMAs,
+        // the same bits), so that they need not stay in registers past the weights.
+        ps = weights();
+        if (__builtin_amdgcn_ballot_w64(!(ps <= __builtin_exp2f(kSlack))) != 0 && rescale())
+          ps = weights();
+      } else {
+        rescale();
+        ps = weights();
       }
-      float pz[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = EB == 2 ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], zsp, -m[c]))
-                                : __builtin_amdgcn_exp2f(z[i] - m[c]);
-        pz[i] = ok[i] ? e : 0.0f;
-        lsum[c] += pz[i];
-      }
+      lsum[c] += ps;
       // P^T: one fp16 operand, or bf16 hi part + remainder
       uint32_t phw[4], plw[4];
 #pragma unroll
