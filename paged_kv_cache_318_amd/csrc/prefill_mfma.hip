@@ -79,7 +79,7 @@ __device__ int seq_by_length_rank(const int32_t* lens, int S, int r, int lane, i
 }
 
 // Three wave64s per SIMD (at most 168 registers a lane): the two-column-set instances at D = 128
-// need a few more, and the compiler spills 5 of them around the second loop, never inside
+// need a few more, and the compiler spills 4 or 5 of them around the second loop, never inside
 // either loop (two waves per SIMD with no spill ran 5% slower).
 template <int CDT, int QDT, int D, int B>
 __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(PrefillArgs a) {
@@ -423,8 +423,7 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(PrefillArgs a) {
         // Weights first: while every lane's 8 weights sum to at most 2^kSlack (so each is at
         // most that), the max is not needed at all. Otherwise (a large score, the first
         // iteration's -inf max, or inf / NaN) the max decides, and the weights are taken again
-        // if it moved. That rare path takes the set's scores again from LDS (the same MFMAs,
-        // the same bits), so that they need not stay in registers past the weights.
+        // if it moved.
         ps = weights();
         if (__builtin_amdgcn_ballot_w64(!(ps <= __builtin_exp2f(kSlack))) != 0 && rescale())
           ps = weights();
