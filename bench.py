@@ -2,8 +2,10 @@
 """Benchmark of one decode step of paged attention on one MI355X.
 
 A step is the whole hot path for one layer over one batch: copy-on-write block copies (when the
-workload has any), the slot-mapped write of every sequence's new token, then decode attention
-through the block tables (partition kernel + merge). The default workload is the OPT-13B-shaped
+workload has any), the slot-mapped write of every sequence's new token and decode attention
+through the block tables. By default the write rides along with the attention in one launch
+(pa_decode_append; the grid's last work-groups store the new tokens), then the merge when a
+sequence spans several partitions; ``--separate`` times pa_write_kv, then pa_decode instead. The default workload is the OPT-13B-shaped
 MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
 uniform in [128, 2048], blocks scattered through a pool with 20% free blocks.
 
@@ -56,9 +58,9 @@ def parse_args():
                    help="time budget of each leg of the oracle timing (all cores, one thread)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
-    p.add_argument("--fused", action="store_true",
-                   help="step through pa_decode_append (the write rides along with the attention) "
-                        "instead of pa_write_kv + pa_decode")
+    p.add_argument("--separate", action="store_true",
+                   help="step through pa_write_kv, then pa_decode, instead of pa_decode_append (the "
+                        "write riding along with the attention, the default)")
     p.add_argument("--num-seqs", type=int, default=0,
                    help="configs 2, 3, 5: use only this many sequences (a smaller batch)")
     p.add_argument("--grouped", action="store_true",
@@ -509,6 +511,7 @@ def prepare_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fu
     kernel = "decode_mfma" if (grouped or variant == 2 or (variant == 0 and mfma_ok and G >= 2)) \
         else "decode_valu"
     return {"w": w, "step": step, "buffers": [reps, out, ws, gr], "kernel": kernel, "shared": shared,
+            "fused": fused and gr is None,
             "grouped": None if gr is None else
             {"groups": gr["groups"], "max_prefix_blocks": gr["max_prefix_blocks"]}}
 
@@ -574,10 +577,11 @@ def us(ms):
     return None if ms is None else round(1e3 * ms, 2)
 
 
-def decode_roofline(w, m, unique):
+def decode_roofline(w, m, unique, fused):
     """Achieved algorithmic GB/s of the attention kernel (average launch) and its fraction of the
-    8 TB/s HBM peak."""
-    dec = w.decode_bytes(unique=unique)
+    8 TB/s HBM peak. A fused launch (pa_decode_append) also moves the new tokens: their bytes are
+    counted with it."""
+    dec = w.decode_bytes(unique=unique) + (w.write_bytes() if fused else 0)
     achieved = dec / (m["kernels_ms"]["decode_partition"] * 1e-3) / 1e9
     return dec, achieved, achieved / HBM_PEAK_GBS
 
@@ -610,10 +614,12 @@ def measure_also(args, lib, torch, preps):
     for (label, n, over, grouped, unique), prep in zip(ALSO, preps):
         w = prep["w"]
         m = time_steps(prep, also_args, lib, torch)
-        dec, achieved, frac = decode_roofline(w, m, unique)
+        dec, achieved, frac = decode_roofline(w, m, unique, prep["fused"])
         step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
         res[label] = {
-            "kernel": m["kernel"], "decode": "pa_decode_grouped" if grouped else "pa_decode",
+            "kernel": m["kernel"],
+            "decode": "pa_decode_grouped" if grouped else
+                      ("pa_decode_append" if prep["fused"] else "pa_decode"),
             "attention_kernel_us": us(m["kernels_ms"]["decode_partition"]),
             "merge_us": us(m["kernels_ms"]["decode_merge"]),
             "write_kv_us": us(m["kernels_ms"]["write_kv"]),
@@ -681,9 +687,10 @@ def main():
     calibration_copy(args, torch)
     # every workload is on the device before the first timed step; the others are timed right
     # after the headline one
+    fused = not args.separate
     prep = prepare_steps(w, args, lib, torch, grouped=args.grouped, variant=args.variant,
-                         partition=args.partition, fused=args.fused)
-    also_preps = [prepare_steps(x, args, lib, torch, grouped=g)
+                         partition=args.partition, fused=fused)
+    also_preps = [prepare_steps(x, args, lib, torch, grouped=g, fused=fused)
                   for x, (_, _, _, g, _) in zip(also_ws, ALSO)]
     del also_ws
     m = time_steps(prep, args, lib, torch)
@@ -691,7 +698,8 @@ def main():
     step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
     unique = args.config == 4
-    dec_bytes, achieved, frac = decode_roofline(w, m, unique)
+    fused = prep["fused"]
+    dec_bytes, achieved, frac = decode_roofline(w, m, unique, fused)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -716,7 +724,7 @@ def main():
             "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
             "replicas": args.replicas, "partition_tokens": args.partition, "variant": args.variant,
             "shared_blocks_flag": m["shared"],
-            "write": "fused into the attention (pa_decode_append)" if args.fused
+            "write": "fused into the attention (pa_decode_append)" if fused
                      else "separate launch (pa_write_kv, then pa_decode)",
             "grouped": m["grouped"],
         },

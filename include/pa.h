@@ -249,9 +249,13 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
  * [Wikipedia] "Математическая формулировка": the query attends every cached token including its
  * own), bit for bit. The new token of sequence s is its position context_lens[s] - 1: the
  * work-group that loads that position's block puts the new key and value (fp8: quantised with the
- * block's scale exactly as pa_write_kv stores them) into the loaded tile in its registers, and
- * stores the key row and the block's whole value tile back, so no separate write launch precedes
- * the attention.
+ * block's scale exactly as pa_write_kv stores them) into the loaded tile in its registers, so no
+ * separate write launch precedes the attention. Who stores the token into the cache: with the
+ * vector-ALU kernel on its ordered 1-D grid, extra work-groups at the end of the grid, which the
+ * hardware dispatches after all the attention's (they run in its drain and store each token as
+ * pa_write_kv does); otherwise (the matrix-core kernel, or a 3-D grid: partitions shorter than
+ * 1024 tokens, more sequences than the ordered list holds, or PA_DECODE_SHARED_BLOCKS) the
+ * work-group holding the block, which stores the key row and the block's whole value tile back.
  *
  *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim] in new_dtype: the cache dtype for a
  *                 16/32-bit cache, q_dtype for an fp8 cache.

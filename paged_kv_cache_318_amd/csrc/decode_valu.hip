@@ -49,6 +49,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane >> 4, c = lane & 15;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+  if (a.tail_wgs > 0 && static_cast<int>(blockIdx.x) >= a.tail_from) {  // pa_decode_append's writes
+    tail_write<CDT, CDT == DT_FP8 ? QDT : CDT, D, B>(a, static_cast<int>(blockIdx.x) - a.tail_from);
+    return;
+  }
 
   int h, s, p, L;
   if (a.ordered) {
@@ -80,8 +84,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int g = h / (Hq / Hkv);
   // pa_decode_append: the partition holding the last block substitutes the new token (position
   // L-1, offset o_new of that block) for what the cache holds there, in the registers its tile
-  // was loaded into, and -- one work-group per kv head -- stores the key row and the whole value
-  // tile back (whole lines rather than one element per dim row).
+  // was loaded into. Without tail writers (3-D grid) it also -- one work-group per kv head --
+  // stores the key row and the whole value tile back (whole lines rather than one element per
+  // dim row).
   constexpr int NDT = CDT == DT_FP8 ? QDT : CDT;  // dtype of the new rows
   constexpr int NEB = Elem<NDT>::bytes;
   const int slot_new = (a.new_slots != nullptr && b1 == nblk) ? new_token_slot(a, s, L, B) : -1;
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int jj = 0; jj < DPL; ++jj) put_elem<EB>(vr[u][jj], en, new_value_bits<CDT, NDT>(vnew[jj], vsc));
       }
-      if (writer) {
+      if (writer && a.tail_wgs == 0) {
         const size_t base = (static_cast<size_t>(pb) * Hkv + g) * tile;
         uint8_t* kt = const_cast<uint8_t*>(a.k_cache) + base;
         uint8_t* vt = const_cast<uint8_t*>(a.v_cache) + base;
@@ -397,9 +402,12 @@ static hipError_t launch_valu_d(const DecodeArgs& a, int D, int B, dim3 grid, hi
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int cdt, int qdt, int D, int B, hipStream_t st) {
-  const dim3 grid = a.ordered ? dim3(static_cast<unsigned>(xcd_weighted_grid(
-                                    static_cast<long long>(a.num_heads) * a.num_seqs * a.max_parts)))
+hipError_t launch_decode_valu(const DecodeArgs& a0, int cdt, int qdt, int D, int B, hipStream_t st) {
+  DecodeArgs a = a0;
+  a.tail_from = 0;
+  a.tail_wgs = 0;
+  const dim3 grid = a.ordered ? dim3(add_tail_writers(a, static_cast<unsigned>(xcd_weighted_grid(
+                                    static_cast<long long>(a.num_heads) * a.num_seqs * a.max_parts)), D))
                               : dim3(a.num_heads, a.num_seqs, a.max_parts);
   if (cdt == DT_F32 && qdt == DT_F32) return launch_valu_d<DT_F32, DT_F32>(a, D, B, grid, st);
   if (cdt == DT_F16 && qdt == DT_F16) return launch_valu_d<DT_F16, DT_F16>(a, D, B, grid, st);

@@ -81,6 +81,31 @@ __device__ __forceinline__ int new_token_slot(const DecodeArgs& a, int s, int L,
   return (slot >= 0 && pb >= 0 && pb < a.num_blocks && slot == pb * B + (L - 1) % B) ? slot : -1;
 }
 
+// The slot writes of pa_decode_append done by the grid's tail: thread x of the a.tail_wgs
+// work-groups (w = its work-group's place among them) takes the (sequence, kv head, 8-dim piece)
+// items x, x + 256 * tail_wgs, ... and writes each piece whose sequence's new token the attention
+// takes along (new_token_slot), with pa_write_kv's own piece write, so the cache ends as
+// pa_write_kv leaves it. Nothing else of the launch reads those slots: the work-group that loads
+// a new token's block puts the token in from k_new / v_new instead.
+template <int CDT, int NDT, int D, int B>
+__device__ void tail_write(const DecodeArgs& a, int w) {
+  constexpr int kPieces = D / 8;
+  const long long total = static_cast<long long>(a.num_seqs) * a.num_kv_heads * kPieces;
+  const long long stride = static_cast<long long>(a.tail_wgs) * blockDim.x;
+  for (long long x = static_cast<long long>(w) * blockDim.x + threadIdx.x; x < total; x += stride) {
+    const int d0 = static_cast<int>(x % kPieces) * 8;
+    const long long sh = x / kPieces;
+    const int hh = static_cast<int>(sh % a.num_kv_heads), s = static_cast<int>(sh / a.num_kv_heads);
+    int L = a.lens[s];
+    L = L < 0 ? 0 : (L > a.max_blocks * B ? a.max_blocks * B : L);
+    const int slot = new_token_slot(a, s, L, B);
+    if (slot < 0) continue;
+    write_piece<NDT, CDT, true>(a.k_new, a.v_new, const_cast<uint8_t*>(a.k_cache),
+                                const_cast<uint8_t*>(a.v_cache), s, slot, hh, d0, a.num_kv_heads,
+                                D, B, a.k_scale, a.v_scale);
+  }
+}
+
 // A new token's key piece of N elements (raw input of type NDT) in the cache's representation:
 // the input bits for a 16/32-bit cache; for an fp8 cache the E4M3 codes of x / scale, as the
 // write kernel stores them.

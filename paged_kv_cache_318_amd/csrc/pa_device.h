@@ -226,10 +226,14 @@ struct DecodeArgs {
   float zscale;    // softmax scale * log2(e)
   // pa_decode_append: the batch's new tokens ([S][Hkv][D], the cache dtype, or the query dtype for
   // an fp8 cache) and their slots; each kernel takes sequence s's new token from here at position
-  // L-1 and the work-group holding its block writes it into the cache. nullptr: plain decode.
+  // L-1. With tail_wgs > 0 (the vector-ALU kernel's ordered 1-D grid) the last tail_wgs
+  // work-groups (from index tail_from on; the hardware dispatches them last) write the new tokens
+  // into the cache; otherwise the work-group holding the token's block does. nullptr: plain
+  // decode.
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  int tail_from, tail_wgs;
   // pa_decode_grouped: sequences group_start[i] .. group_start[i+1]-1 form group i and share
   // their first prefix_blocks[s] table entries. Partial results then sit in one slot per
   // (sequence, query head, part): ws_o[(s * Hq + h) * max_parts + k][D] (heads_per_unit 1), the

@@ -28,6 +28,23 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStre
   hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev.start, ev.stop, 0u, args...);
 }
 
+// pa_decode_append on a 1-D grid of grid_x work-groups: appends the work-groups that write the
+// new tokens into the cache (one per 1024 (sequence, kv head, 8-dim piece) items; the hardware
+// dispatches them after all the attention's, so they run in the launch's drain) and returns the
+// grown grid. Plain decode, or a grid that would outgrow the launch limit, keeps grid_x and
+// tail_wgs = 0 (then the attention's own work-groups write).
+inline unsigned add_tail_writers(DecodeArgs& a, unsigned grid_x, int head_dim) {
+  a.tail_from = 0;
+  a.tail_wgs = 0;
+  if (a.new_slots == nullptr) return grid_x;
+  const long long pieces = static_cast<long long>(a.num_seqs) * a.num_kv_heads * (head_dim / 8);
+  const long long wgs = (pieces + 1023) / 1024;
+  if (static_cast<long long>(grid_x) + wgs > 0xFFFFFFFFLL / 256) return grid_x;
+  a.tail_from = static_cast<int>(grid_x);
+  a.tail_wgs = static_cast<int>(wgs);
+  return grid_x + static_cast<unsigned>(wgs);
+}
+
 hipError_t launch_decode_valu(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,
                               int block_size, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int cache_dt, int q_dt, int head_dim,

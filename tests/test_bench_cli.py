@@ -23,7 +23,7 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_measurements():
     p = _run("--help")
     assert p.returncode == 0
-    for word in ("--config", "--measure", "--fused", "--grouped", "--partition"):
+    for word in ("--config", "--measure", "--separate", "--grouped", "--partition"):
         assert word in p.stdout
 
 

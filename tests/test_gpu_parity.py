@@ -130,11 +130,16 @@ def test_config1_tiny_fp32():
 
 
 def _bench_launch_and_fused(w, out_dt, **kw):
-    """The step as bench.py times it (pa_write_kv, then pa_decode with the default plan), and the
-    fused step (pa_decode_append), which must give the same bits."""
-    sep = run_gpu(w, out_dt=out_dt, fused=False, **kw)
-    assert np.array_equal(sep, run_gpu(w, out_dt=out_dt, fused=True, **kw))
-    return sep
+    """The step as bench.py times it (pa_decode_append with the default plan: the last
+    work-groups of its grid write the new tokens), and the separate write + decode (pa_write_kv,
+    then pa_decode): outputs and caches bit for bit equal."""
+    fus, df = run_gpu(w, out_dt=out_dt, fused=True, return_pools=True, **kw)
+    sep, ds = run_gpu(w, out_dt=out_dt, fused=False, return_pools=True, **kw)
+    assert np.array_equal(sep, fus)
+    for a, b in ((ds.k_cache, df.k_cache), (ds.v_cache, df.v_cache)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    del df, ds
+    return fus
 
 
 @pytest.mark.parametrize("out_dt", ["f16", "f32"])
