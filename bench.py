@@ -4,8 +4,8 @@
 A step is the whole hot path for one layer over one batch: copy-on-write block copies (when the
 workload has any), the slot-mapped write of every sequence's new token and decode attention
 through the block tables. By default the write rides along with the attention in one launch
-(pa_decode_append; the grid's last work-groups store the new tokens), then the merge when a
-sequence spans several partitions; ``--separate`` times pa_write_kv, then pa_decode instead. The default workload is the OPT-13B-shaped
+(pa_decode_append, or pa_decode_grouped_append with --grouped), then the merge when a sequence
+spans several partitions; ``--separate`` times pa_write_kv, then the decode, instead. The default workload is the OPT-13B-shaped
 MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
 uniform in [128, 2048], blocks scattered through a pool with 20% free blocks.
 
@@ -59,8 +59,9 @@ def parse_args():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also launch one plain device copy of this many MiB (counter calibration)")
     p.add_argument("--separate", action="store_true",
-                   help="step through pa_write_kv, then pa_decode, instead of pa_decode_append (the "
-                        "write riding along with the attention, the default)")
+                   help="step through pa_write_kv, then the decode, instead of pa_decode_append / "
+                        "pa_decode_grouped_append (the write riding along with the attention, the "
+                        "default)")
     p.add_argument("--num-seqs", type=int, default=0,
                    help="configs 2, 3, 5: use only this many sequences (a smaller batch)")
     p.add_argument("--grouped", action="store_true",
@@ -500,7 +501,7 @@ def prepare_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fu
             decode_step_grouped(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new,
                                 d.slots, d.cow, gr["gs"], gr["pref"], gr["mg"], w.scale,
                                 d.k_scale, d.v_scale, partition_tokens=partition,
-                                workspace=gr["ws"], flags=flags)
+                                workspace=gr["ws"], flags=flags, fused=fused)
             return
         decode_step(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new, d.slots,
                     d.cow, w.scale, d.k_scale, d.v_scale, partition_tokens=partition,
@@ -511,7 +512,7 @@ def prepare_steps(w, args, lib, torch, grouped=False, variant=0, partition=0, fu
     kernel = "decode_mfma" if (grouped or variant == 2 or (variant == 0 and mfma_ok and G >= 2)) \
         else "decode_valu"
     return {"w": w, "step": step, "buffers": [reps, out, ws, gr], "kernel": kernel, "shared": shared,
-            "fused": fused and gr is None,
+            "fused": fused,
             "grouped": None if gr is None else
             {"groups": gr["groups"], "max_prefix_blocks": gr["max_prefix_blocks"]}}
 
@@ -618,8 +619,8 @@ def measure_also(args, lib, torch, preps):
         step_bytes = w.decode_bytes() + w.write_bytes() + w.copy_bytes()
         res[label] = {
             "kernel": m["kernel"],
-            "decode": "pa_decode_grouped" if grouped else
-                      ("pa_decode_append" if prep["fused"] else "pa_decode"),
+            "decode": ("pa_decode_grouped" if grouped else "pa_decode") +
+                      ("_append" if prep["fused"] else ""),
             "attention_kernel_us": us(m["kernels_ms"]["decode_partition"]),
             "merge_us": us(m["kernels_ms"]["decode_merge"]),
             "write_kv_us": us(m["kernels_ms"]["write_kv"]),
@@ -724,8 +725,9 @@ def main():
             "decode_bytes": w.decode_bytes(), "unique_decode_bytes": w.decode_bytes(unique=True),
             "replicas": args.replicas, "partition_tokens": args.partition, "variant": args.variant,
             "shared_blocks_flag": m["shared"],
-            "write": "fused into the attention (pa_decode_append)" if fused
-                     else "separate launch (pa_write_kv, then pa_decode)",
+            "write": ("fused into the attention (pa_decode_grouped_append)" if args.grouped
+                      else "fused into the attention (pa_decode_append)") if fused
+                     else "separate launch (pa_write_kv, then the decode)",
             "grouped": m["grouped"],
         },
         "kernels_us": {

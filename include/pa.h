@@ -243,6 +243,29 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_grouped_append -- pa_decode_grouped with the step's slot write taken along, as
+ * pa_decode_append takes it along with pa_decode ([Ultralytics] "ページングの仕組み": the new
+ * token goes to its slot): the same result, in the cache and in `out`, as pa_write_kv(k_new,
+ * v_new, ..., slot_mapping, num_tokens = num_seqs) followed by pa_decode_grouped, bit for bit.
+ * The work-group holding a sequence's own last block (never a shared one: copy-on-write gives the
+ * block the step writes into to one sequence) puts the new key and value into its loaded tile
+ * and stores the key row and the block's value tile back.
+ *
+ *   k_new, v_new, slot_mapping, new_dtype  as for pa_decode_append.
+ *   everything else as for pa_decode_grouped (same workspace size).
+ */
+int pa_decode_grouped_append(void* out, const void* q, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                             pa_dtype new_dtype, const int32_t* group_start,
+                             const int32_t* prefix_blocks, int num_groups, int max_group_size,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                             pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                             const float* k_scale, const float* v_scale, int partition_tokens,
+                             int flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_append -- the slot write and the decode of one step in one pass: the same result, in
  * the cache and in `out`, as pa_write_kv(k_new, v_new, ..., slot_mapping, num_tokens = num_seqs)
  * followed by pa_decode ([Ultralytics] "ページングの仕組み": the new token goes to its slot;

@@ -120,9 +120,11 @@ __device__ __forceinline__ void mfma_segment(const DecodeArgs& a, float* smem, i
   // pa_decode_append: the segment holding the unit's last block substitutes the new token
   // (position L-1, row o_new of its tile) for what the cache holds there -- in the staged key
   // tile and in the value registers -- and stores the key row and the value tile rows of its
-  // block back (whole lines rather than one element per dim row).
+  // block back (whole lines rather than one element per dim row). A segment whose rows are
+  // several sequences' (a group's shared prefix) holds no sequence's own last block.
   const int nblk_all = (L + B - 1) / B;
-  const int slot_new = (a.new_slots != nullptr && b1 == nblk_all) ? new_token_slot(a, s, L, B) : -1;
+  const int slot_new = (a.new_slots != nullptr && b1 == nblk_all && rows == G)
+                           ? new_token_slot(a, s, L, B) : -1;
   const int item_new = (nblk_all - 1 - b0) / GB;  // (meaningful only when slot_new >= 0)
   const int sub_new = PAIR ? 0 : ((L - 1) % B) / 16;
   const int o_new = (L - 1) - tile_start(item_new, sub_new);

@@ -537,14 +537,17 @@ size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_heads, int head_d
                            grouped_plan(max_blocks_per_seq, block_size, partition_tokens));
 }
 
-int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens,
-                      const int32_t* group_start, const int32_t* prefix_blocks, int num_groups,
-                      int max_group_size, int num_seqs, int num_heads, int num_kv_heads,
-                      int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
-                      float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
-                      const float* k_scale, const float* v_scale, int partition_tokens, int flags,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+// pa_decode_grouped, and pa_decode_grouped_append when k_new != nullptr (new tokens taken along
+// and written by the work-group holding each sequence's last block).
+static int grouped_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* group_start, const int32_t* prefix_blocks, int num_groups,
+                        int max_group_size, int num_seqs, int num_heads, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                        float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                        const float* k_scale, const float* v_scale, int partition_tokens, int flags,
+                        void* workspace, size_t workspace_bytes, void* stream, const void* k_new,
+                        const void* v_new, const int32_t* slot_mapping) {
   if (num_groups <= 0 || max_group_size <= 0 || num_groups > num_seqs) return PA_ERR_INVALID_ARG;
   const int status = check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                        num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -590,6 +593,9 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
   a.num_groups = num_groups;
   a.group_start = group_start;
   a.prefix_blocks = prefix_blocks;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = k_new != nullptr ? slot_mapping : nullptr;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPair ev;
@@ -601,6 +607,42 @@ int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void*
   e = pa::launch_decode_merge(a, head_dim, block_size, st);
   end_event(timed, st, ev, PA_KERNEL_DECODE_MERGE);
   return hip_status(e);
+}
+
+int pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* group_start, const int32_t* prefix_blocks, int num_groups,
+                      int max_group_size, int num_seqs, int num_heads, int num_kv_heads,
+                      int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                      float scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                      const float* k_scale, const float* v_scale, int partition_tokens, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_impl(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
+                      prefix_blocks, num_groups, max_group_size, num_seqs, num_heads, num_kv_heads,
+                      head_dim, block_size, max_blocks_per_seq, num_blocks, scale, q_dtype,
+                      cache_dtype, out_dtype, k_scale, v_scale, partition_tokens, flags, workspace,
+                      workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+int pa_decode_grouped_append(void* out, const void* q, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                             pa_dtype new_dtype, const int32_t* group_start,
+                             const int32_t* prefix_blocks, int num_groups, int max_group_size,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                             pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                             const float* k_scale, const float* v_scale, int partition_tokens,
+                             int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(new_dtype) || !dtype_ok(cache_dtype) || !dtype_ok(q_dtype)) return PA_ERR_INVALID_ARG;
+  // the new rows are stored as they are (16-bit caches) or quantised from the query type (fp8)
+  if (new_dtype != (cache_dtype == PA_FP8_E4M3 ? q_dtype : cache_dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  return grouped_impl(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
+                      prefix_blocks, num_groups, max_group_size, num_seqs, num_heads, num_kv_heads,
+                      head_dim, block_size, max_blocks_per_seq, num_blocks, scale, q_dtype,
+                      cache_dtype, out_dtype, k_scale, v_scale, partition_tokens, flags, workspace,
+                      workspace_bytes, stream, k_new, v_new, slot_mapping);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -47,6 +47,9 @@ _SIGS = {
     "pa_decode_grouped": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                            _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _i32, _i32,
                            _vp, _sz, _vp], _i32),
+    "pa_decode_grouped_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                  _i32, _vp, _vp, _i32, _i32, _vp, _sz, _vp], _i32),
     "pa_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _i32, _f32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "pa_swap_blocks": ([_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
@@ -303,6 +306,36 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, grou
         _ptr(group_start), _ptr(prefix_blocks), group_start.shape[0] - 1, int(max_group_size), S, Hq,
         Hkv, D, B, MB, NB, float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out),
         _ptr(k_scale), _ptr(v_scale), int(partition_tokens), int(flags), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def pa_decode_grouped_append(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
+                             slot_mapping, group_start, prefix_blocks, max_group_size: int,
+                             scale: float, k_scale=None, v_scale=None, partition_tokens: int = 0,
+                             workspace=None, stream=None, flags: int = 0) -> None:
+    """pa_write_kv of one new token per sequence (as pa_decode_append) and pa_decode_grouped in
+    one pass."""
+    import torch
+    NB, Hkv, B, D = k_cache.shape
+    S, Hq, Dq = q.shape
+    MB = block_tables.shape[1]
+    _need(Dq == D and tuple(out.shape) == (S, Hq, D), "q/out must be [S][Hq][D]")
+    _need(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [NB][Hkv][D][B]")
+    _need(tuple(k_new.shape) == (S, Hkv, D) and k_new.shape == v_new.shape,
+          "k_new/v_new must be [S][Hkv][D]")
+    _need(all(t.dtype == torch.int32 for t in (block_tables, context_lens, slot_mapping,
+                                                 group_start, prefix_blocks)),
+          "block_tables / context_lens / slot_mapping / group_start / prefix_blocks must be int32")
+    _need(block_tables.shape[0] == S and context_lens.shape[0] == S and slot_mapping.shape[0] == S
+          and prefix_blocks.shape[0] == S, "one table row / length / slot / prefix per sequence")
+    _need(group_start.dim() == 1 and group_start.shape[0] >= 2, "group_start must be [groups + 1]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_grouped_append", load().pa_decode_grouped_append(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), dtype_code(k_new), _ptr(group_start),
+        _ptr(prefix_blocks), group_start.shape[0] - 1, int(max_group_size), S, Hq, Hkv, D, B, MB, NB,
+        float(scale), dtype_code(q), dtype_code(k_cache), dtype_code(out), _ptr(k_scale),
+        _ptr(v_scale), int(partition_tokens), int(flags), _ptr(workspace), ws_bytes,
         _stream(stream)))
 
 

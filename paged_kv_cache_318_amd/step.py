@@ -57,15 +57,23 @@ def grouped_workspace_for(q, block_tables, block_size: int, partition_tokens: in
 def decode_step_grouped(out, q, k_cache, v_cache, block_tables, context_lens, k_new, v_new,
                         slot_mapping, cow_pairs, group_start, prefix_blocks, max_group_size: int,
                         scale: float, k_scale=None, v_scale=None, partition_tokens: int = 0,
-                        workspace=None, stream=None, flags: int = 0) -> None:
+                        workspace=None, stream=None, flags: int = 0, fused: bool = True) -> None:
     """The decode step of a batch whose sequences share prefix blocks (``group_start`` /
-    ``prefix_blocks`` as ``blocks.shared_prefix_groups`` returns them, on the GPU): copies, the
-    slot write, then pa_decode_grouped, which reads each shared block once per group."""
+    ``prefix_blocks`` as ``blocks.shared_prefix_groups`` returns them, on the GPU): copies, then
+    pa_decode_grouped, which reads each shared block once per group, with the slot write taken
+    along (``fused``: pa_decode_grouped_append) or as pa_write_kv before it."""
     if cow_pairs is not None and cow_pairs.shape[0] > 0:
         lib.pa_copy_blocks(k_cache, v_cache, cow_pairs, k_scale, v_scale, stream=stream)
-    lib.pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=stream)
     if workspace is None:
         workspace = grouped_workspace_for(q, block_tables, k_cache.shape[2], partition_tokens)
+    if fused:
+        lib.pa_decode_grouped_append(out, q, k_cache, v_cache, block_tables, context_lens, k_new,
+                                     v_new, slot_mapping, group_start, prefix_blocks,
+                                     max_group_size, scale, k_scale, v_scale,
+                                     partition_tokens=partition_tokens, workspace=workspace,
+                                     stream=stream, flags=flags)
+        return
+    lib.pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=stream)
     lib.pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
                           prefix_blocks, max_group_size, scale, k_scale, v_scale,
                           partition_tokens=partition_tokens, workspace=workspace, stream=stream,

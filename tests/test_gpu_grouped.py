@@ -36,9 +36,10 @@ def share_prefixes(w, group_size):
     return w
 
 
-def run_grouped(w, out_dt="f32", part=0, max_group_size=4, flags=0):
-    """Copies and the slot write as a step does, then pa_decode_grouped with the groups the host
-    helper finds in the step's tables."""
+def run_grouped(w, out_dt="f32", part=0, max_group_size=4, flags=0, fused=True, return_pools=False):
+    """Copies as a step does, then the grouped decode with the groups the host helper finds in the
+    step's tables: the slot write taken along (pa_decode_grouped_append), or with ``fused=False``
+    pa_write_kv, then pa_decode_grouped."""
     _check_inputs(w)
     d = upload(w)
     gs, pref = shared_prefix_groups(w.tables, w.lens, w.block_size, max_group_size)
@@ -46,9 +47,22 @@ def run_grouped(w, out_dt="f32", part=0, max_group_size=4, flags=0):
     decode_step_grouped(out, d.q, d.k_cache, d.v_cache, d.tables, d.lens, d.k_new, d.v_new,
                         d.slots, d.cow, torch.from_numpy(gs).cuda(), torch.from_numpy(pref).cuda(),
                         max_group_size, w.scale, d.k_scale, d.v_scale, partition_tokens=part,
-                        flags=flags)
+                        flags=flags, fused=fused)
     torch.cuda.synchronize()
+    if return_pools:
+        return to_numpy_f64(out), gs, pref, d
     return to_numpy_f64(out), gs, pref
+
+
+def _fused_matches_separate(w, **kw):
+    """pa_decode_grouped_append against pa_write_kv + pa_decode_grouped: outputs and caches bit
+    for bit equal."""
+    fus, gs, pref, df = run_grouped(w, return_pools=True, **kw)
+    sep, _, _, ds = run_grouped(w, fused=False, return_pools=True, **kw)
+    assert np.array_equal(fus, sep)
+    for a, b in ((ds.k_cache, df.k_cache), (ds.v_cache, df.v_cache)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    return fus, gs, pref
 
 
 @pytest.mark.parametrize("flags", [0, lib.PA_DECODE_SHARED_BLOCKS])
@@ -56,7 +70,7 @@ def test_shared_prefix_batch(flags):
     """The shared-prefix sampling batch (16 prompts x 4 samples, 40 heads): four-member groups
     sharing each prompt's whole blocks; against the oracle and against pa_decode."""
     w = cfg(4)
-    got, gs, pref = run_grouped(w, max_group_size=4, flags=flags)
+    got, gs, pref = _fused_matches_separate(w, max_group_size=4, flags=flags)
     assert len(gs) == 17 and pref.min() > 0
     assert_close(got, cfg_ref(4), "bf16", "f32", "grouped cfg4")
     assert np.max(np.abs(got - run_gpu(w, out_dt="f32", flags=flags))) <= TOL["bf16"]
@@ -93,7 +107,7 @@ def test_grouped_parity(cdt, qdt, hq, hkv, D, B, part, samples):
     w = share_prefixes(make_workload(lens, num_heads=hq, num_kv_heads=hkv, head_dim=D, block_size=B,
                                      dtype=cdt, q_dtype=qdt, seed=hq + D + B + part), samples)
     ref = run_oracle(w)
-    got, gs, pref = run_grouped(w, part=part, max_group_size=samples)
+    got, gs, pref = _fused_matches_separate(w, part=part, max_group_size=samples)
     assert pref.max() > 0
     assert_close(got, ref, cdt, "f32", f"grouped {cdt} Hq={hq} Hkv={hkv} D={D} B={B} part={part}")
     got16, _, _ = run_grouped(w, out_dt=qdt, part=part, max_group_size=samples)
@@ -105,7 +119,7 @@ def test_grouped_without_sharing_and_empty_sequences():
     lens = [0, 5, 300, 0, 17, 1000]
     w = make_workload(lens, num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=3)
     w.slots[np.asarray(lens) == 0] = -1
-    got, gs, pref = run_grouped(w, max_group_size=4)  # 4 members x 4 heads = 16 rows
+    got, gs, pref = _fused_matches_separate(w, max_group_size=4)  # 4 members x 4 heads = 16 rows
     assert pref.max() == 0
     ref = run_oracle(w)
     assert_close(got, ref, "bf16", "f32", "grouped, nothing shared")
