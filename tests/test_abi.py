@@ -47,7 +47,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("pa_write_kv", "pa_decode", "pa_decode_append", "pa_prefill", "pa_copy_blocks",
               "pa_gather_kv",
-              "pa_swap_blocks", "pa_decode_grouped", "pa_decode_grouped_workspace_bytes",
+              "pa_swap_blocks", "pa_decode_grouped", "pa_decode_grouped_append",
+              "pa_decode_grouped_workspace_bytes",
               "pa_decode_workspace_bytes", "pa_status_string", "pa_decode_noalloc"):
         assert n in names
 
@@ -263,6 +264,33 @@ def test_decode_append_rejects_bad_arguments(L, kw, want):
     """The new rows' dtype must be the cache dtype (the query dtype for an fp8 cache); every other
     check is pa_decode's."""
     assert _append(L, **kw) == want
+
+
+def _grouped_append(L, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tab=FAKE, lens=FAKE, kn=FAKE, vn=FAKE, slots=FAKE,
+             ndt=BF16, gs=FAKE, pref=FAKE, ng=2, mg=4, S=8, Hq=8, Hkv=2, D=128, B=16, MB=8, NB=64,
+             scale=0.1, qdt=BF16, cdt=BF16, odt=F32, ks=None, vs=None, part=0, flags=0, ws=None,
+             wsb=0)
+    a.update(kw)
+    return L.pa_decode_grouped_append(
+        a["out"], a["q"], a["kc"], a["vc"], a["tab"], a["lens"], a["kn"], a["vn"], a["slots"],
+        a["ndt"], a["gs"], a["pref"], a["ng"], a["mg"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+        a["MB"], a["NB"], a["scale"], a["qdt"], a["cdt"], a["odt"], a["ks"], a["vs"], a["part"],
+        a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ndt=F16), UNSUPPORTED), (dict(ndt=9), INVALID), (dict(kn=None), INVALID),
+    (dict(vn=None), INVALID), (dict(slots=None), INVALID), (dict(ng=0), INVALID),
+    (dict(ng=9), INVALID), (dict(mg=8), UNSUPPORTED), (dict(gs=None), INVALID),
+    (dict(cdt=F32, qdt=F32, ndt=F32), UNSUPPORTED), (dict(flags=4), INVALID),
+    (dict(), WORKSPACE),  # every argument valid but no workspace: refused before any launch
+])
+def test_decode_grouped_append_rejects_bad_arguments(L, kw, want):
+    """The new rows' checks of pa_decode_append, then pa_decode_grouped's own: groups, rows per
+    matrix-core tile (members x query heads per kv head <= 16), the 16-bit / fp8 caches only, and
+    the workspace."""
+    assert _grouped_append(L, **kw) == want
 
 
 def _prefill(L, **kw):
