@@ -5,8 +5,8 @@ A step is the whole hot path for one layer over one batch: copy-on-write block c
 workload has any), the slot-mapped write of every sequence's new token and decode attention
 through the block tables. By default the write rides along with the attention in one launch
 (pa_decode_append, or pa_decode_grouped_append with --grouped), then the merge when a sequence
-spans several partitions; ``--separate`` times pa_write_kv, then the decode, instead. The default workload is the OPT-13B-shaped
-MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
+spans several partitions; ``--separate`` times pa_write_kv, then the decode, instead. The
+default workload is the OPT-13B-shaped MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
 uniform in [128, 2048], blocks scattered through a pool with 20% free blocks.
 
 Inputs are uploaded before timing (``--replicas`` independent copies of the pools, rotated step by
