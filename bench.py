@@ -6,8 +6,9 @@ workload has any), the slot-mapped write of every sequence's new token and decod
 through the block tables. By default the write rides along with the attention in one launch
 (pa_decode_append, or pa_decode_grouped_append with --grouped), then the merge when a sequence
 spans several partitions; ``--separate`` times pa_write_kv, then the decode, instead. The
-default workload is the OPT-13B-shaped MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16 cache, block size 16, context lengths
-uniform in [128, 2048], blocks scattered through a pool with 20% free blocks.
+default workload is the OPT-13B-shaped MHA decode batch: 64 sequences, 40 heads x 128 dims, fp16
+cache, block size 16, context lengths uniform in [128, 2048], blocks scattered through a pool
+with 20% free blocks.
 
 Inputs are uploaded before timing (``--replicas`` independent copies of the pools, rotated step by
 step, so no step finds the previous step's data in the L2 or the MALL). The timed region is
